@@ -1,0 +1,215 @@
+"""Expert computation on the expanded rows (oracle; test infrastructure only).
+
+Stage order, from SGLang moe_runner/deep_gemm.py source
+(``DeepGemmRunnerCore.run`` -> ``_run_contiguous_gemm``): grouped fp8 GEMM
+with the gate/up weights, SiLU(gate)*up, per-token-group fp8 quantisation,
+grouped fp8 GEMM with the down weights; then the rows of each token are
+combined with their top-k weights.
+
+* Grouped GEMM ("NT", contiguous layout): row ``m`` of the expanded
+  activations is multiplied by the transpose of expert ``m_indices[m]``'s
+  weight matrix; rows labelled -1 are skipped.  Operands are fp8 with 1x128
+  activation scales and 128x128 weight block scales, so the product is the
+  ordinary matmul of the dequantised operands.  Output is bf16.
+  (SGLang moe_runner/deep_gemm.py source, ``_run_contiguous_gemm``: gate_up
+  output ``[all_tokens, N]`` bf16 with ``N = w13.size(1)``, then down output
+  ``[all_tokens, K]`` bf16.)
+* Activation: the first half of the gate_up row is the gate, the second the
+  up projection; ``y = silu(gate) * up`` (same function; the SiTU variant's
+  Triton kernel shows the non-interleaved [gate; up] halves).  ``y`` is
+  quantised per 1x128 group (``quant``).
+* Top-k weight.  In fp32-scale mode each expanded row's top-k weight is
+  folded into the down GEMM's fp32 input scale: the GEMM is linear and fp8
+  dequantisation is code times scale, so scaling the row's scales scales the
+  row's output (SGLang PR 37261, Modifications/Core and the
+  SGLANG_DEEPEP_V2_PREFILL_DO_EXPAND section).  Under power-of-two (UE8M0)
+  scales the weight is applied to the down output instead (same sections).
+  Reading: that post-weighting is done in fp32 inside the gather, before the
+  single bf16 rounding of the combined row.
+* Gather: each token's expert rows are summed back into one row
+  (SGLang moe_runner/deep_gemm.py source, ``post_permute_deep_gemm_to_
+  deepep_v2`` and ``ep_gather`` in ``post_permute_deep_gemm_to_deepep_normal``).
+  Reading: the sum runs over k ascending in fp32, then rounds once to bf16;
+  valid rows with no local slot are zero; rows past the real/padding
+  boundary are not produced (vLLM PR 54109, Design: results for inactive
+  rows only need to be safe to discard).
+
+Precision: the matmuls accumulate in float64 and round once to bf16; the
+activation and quantisation run in float32 (the precision the pages' kernels
+decide fp8 codes in); the gather accumulates in float32.
+"""
+
+import numpy as np
+
+from . import fp8, quant
+from .layout import align_up
+
+
+def grouped_gemm(a_q, a_s, w_q, w_s, m_indices, n_rows: int, fmt: str,
+                 live=None):
+    """out[m] = bf16(deq(a[m]) @ deq(w[m_indices[m]])^T) for m < n_rows with
+    m_indices[m] >= 0 (and live[m], when given).  Other rows are NaN."""
+    w_q = np.asarray(w_q)
+    n_out = w_q.shape[1]
+    out = np.full((n_rows, n_out), np.nan, dtype=np.float32)
+    mi = np.asarray(m_indices)[:n_rows]
+    for e in np.unique(mi[mi >= 0]):
+        sel = mi == e
+        if live is not None:
+            sel &= live
+        rows = np.nonzero(sel)[0]
+        if len(rows) == 0:
+            continue
+        a = quant.dequant_rows(np.asarray(a_q)[rows], np.asarray(a_s)[rows], fmt)
+        w = quant.dequant_block(w_q[e], np.asarray(w_s)[e], fmt)
+        out[rows] = fp8.round_bf16(a @ w.T)
+    return out
+
+
+def silu_mul(g32, u32):
+    """silu(g) * u = g / (1 + exp(-g)) * u, each operation in float32."""
+    g = np.asarray(g32, dtype=np.float32)
+    u = np.asarray(u32, dtype=np.float32)
+    with np.errstate(over="ignore"):
+        den = (np.float32(1.0) + np.exp(-g)).astype(np.float32)
+    return ((g / den).astype(np.float32) * u).astype(np.float32)
+
+
+def live_rows(m_indices, psum, align: int, n_rows: int):
+    """Rows holding a slot: row m of expert e's block is live when it lies
+    below psum[e]; the rest of the block is alignment padding."""
+    mi = np.asarray(m_indices)[:n_rows]
+    live = np.zeros(n_rows, dtype=bool)
+    psum = np.asarray(psum)
+    prev = 0
+    for e in range(len(psum)):
+        start = align_up(prev, align)
+        end = min(int(psum[e]), n_rows)
+        if start < end:
+            live[start:end] = True
+        prev = int(psum[e])
+    return live & (mi >= 0)
+
+
+def act_quant(G, live, fmt: str, fold_weight=None):
+    """SiLU(gate)*up and per-1x128 fp8 quantisation of every live row.
+
+    G: [n, 2I] bf16 values as float32.  Pad rows (not live) get codes 0 and
+    scale 0 (UE8M0 byte 0) without reading G.  With fold_weight ([n] f32,
+    fp32 format only) each live row's scales are multiplied by its weight
+    after the scale is formed."""
+    G = np.asarray(G, dtype=np.float32)
+    n, two_i = G.shape
+    inter = two_i // 2
+    q = np.zeros((n, inter), dtype=np.uint8)
+    s = np.zeros((n, inter // quant.GROUP),
+                 dtype=np.float32 if fmt == "f32" else np.uint8)
+    rows = np.nonzero(live)[0]
+    if len(rows):
+        y = silu_mul(G[rows, :inter], G[rows, inter:])
+        qq, ss = quant.quantize_rows(y, fmt)
+        if fold_weight is not None:
+            if fmt != "f32":
+                raise ValueError("the weight fold needs fp32 scales")
+            ss = (ss * np.asarray(fold_weight, dtype=np.float32)[rows, None]
+                  ).astype(np.float32)
+        q[rows] = qq
+        s[rows] = ss
+    return q, s
+
+
+def gather(D, src2dst, num_valid: int, topk_weights=None):
+    """out[r] = bf16(sum_k c_k * D[src2dst[r, k]]) for r < num_valid, over
+    slots with src2dst >= 0 in ascending k, in float32 (c_k = 1 when
+    topk_weights is None, else topk_weights[r, k]).  Returns [num_valid, H]
+    float32 holding bf16 values."""
+    D = np.asarray(D, dtype=np.float32)
+    src = np.asarray(src2dst)
+    acc = np.zeros((num_valid, D.shape[1]), dtype=np.float32)
+    for k in range(src.shape[1]):
+        d = src[:num_valid, k]
+        ok = d >= 0
+        if not np.any(ok):
+            continue
+        term = D[d[ok]]
+        if topk_weights is not None:
+            c = np.asarray(topk_weights, dtype=np.float32)[:num_valid, k][ok]
+            term = (term * c[:, None]).astype(np.float32)
+        acc[ok] = (acc[ok] + term).astype(np.float32)
+    return fp8.round_bf16(acc)
+
+
+def layer(inp, mode: str = "auto"):
+    """The whole path on one rank.  `inp` holds: x_q [R,H] u8, x_s, ids [R,T],
+    w [R,T] f32, num_valid, w13_q [E,2I,H], w13_s, w2_q [E,H,I], w2_s,
+    align, fmt ('f32' | 'ue8m0'), cap (optional).
+
+    mode: 'fold' (weight folded into the down GEMM's input scales; fp32 only),
+    'post' (weight applied in the gather), or 'auto' (fold for fp32 scales,
+    post for UE8M0, as the pages do).  Returns a dict of every stage."""
+    from .layout import expand, capacity
+    fmt = inp["fmt"]
+    if mode == "auto":
+        mode = "fold" if fmt == "f32" else "post"
+    if mode == "fold" and fmt != "f32":
+        raise ValueError("the weight fold needs fp32 scales")
+    ids = np.asarray(inp["ids"])
+    R, T = ids.shape
+    E = np.asarray(inp["w13_q"]).shape[0]
+    align = int(inp["align"])
+    cap = int(inp.get("cap") or capacity(R, T, E, align))
+    nv = int(inp["num_valid"])
+    lay = expand(ids, inp["w"], inp["x_q"], inp["x_s"], nv, E, align, cap)
+    n = min(lay["total"], cap)
+    live = live_rows(lay["m_indices"], lay["psum"], align, n)
+    G = grouped_gemm(lay["ex"], lay["ex_scale"], inp["w13_q"], inp["w13_s"],
+                     lay["m_indices"], n, fmt, live=live)
+    fold = lay["row_weight"] if mode == "fold" else None
+    dq, ds = act_quant(G, live, fmt, fold_weight=fold)
+    D = grouped_gemm(dq, ds, inp["w2_q"], inp["w2_s"], lay["m_indices"], n,
+                     fmt, live=live)
+    out = gather(D, lay["src2dst"], nv,
+                 topk_weights=None if mode == "fold" else inp["w"])
+    lay.update(G=G, dq=dq, ds=ds, D=D, out=out, live=live, mode=mode, cap=cap)
+    return lay
+
+
+def brute_force(inp, mode: str = "auto"):
+    """Per-token evaluation with no layout: for each valid row r and each
+    slot k naming a local expert, run that expert's MLP on the token with
+    the same roundings as the layered path (bf16 gate_up, fp32 SiLU*up,
+    per-1x128 fp8 quantisation, optional weight fold, bf16 down), and sum
+    the slots in ascending k in fp32 before one bf16 rounding."""
+    fmt = inp["fmt"]
+    if mode == "auto":
+        mode = "fold" if fmt == "f32" else "post"
+    ids = np.asarray(inp["ids"])
+    wts = np.asarray(inp["w"], dtype=np.float32)
+    w13_q, w13_s = np.asarray(inp["w13_q"]), np.asarray(inp["w13_s"])
+    w2_q, w2_s = np.asarray(inp["w2_q"]), np.asarray(inp["w2_s"])
+    E, two_i, H = w13_q.shape
+    inter = two_i // 2
+    nv = int(inp["num_valid"])
+    W13 = [quant.dequant_block(w13_q[e], w13_s[e], fmt) for e in range(E)]
+    W2 = [quant.dequant_block(w2_q[e], w2_s[e], fmt) for e in range(E)]
+    out = np.zeros((nv, H), dtype=np.float32)
+    for r in range(nv):
+        xr = quant.dequant_rows(np.asarray(inp["x_q"])[r:r + 1],
+                                np.asarray(inp["x_s"])[r:r + 1], fmt)
+        acc = np.zeros(H, dtype=np.float32)
+        for k in range(ids.shape[1]):
+            e = int(ids[r, k])
+            if e < 0 or e >= E:
+                continue
+            g = fp8.round_bf16(xr @ W13[e].T)[0]
+            y = silu_mul(g[:inter], g[inter:])
+            q, s = quant.quantize_rows(y[None, :], fmt)
+            if mode == "fold":
+                s = (s * wts[r, k]).astype(np.float32)
+            yq = quant.dequant_rows(q, s, fmt)
+            d = fp8.round_bf16(yq @ W2[e].T)[0]
+            if mode == "post":
+                d = (d * wts[r, k]).astype(np.float32)
+            acc = (acc + d).astype(np.float32)
+        out[r] = fp8.round_bf16(acc)
+    return out
