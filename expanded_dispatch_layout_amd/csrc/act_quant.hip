@@ -1,0 +1,144 @@
+// moe_act_quant: SiLU(gate)*up with per-1x128 fp8 quantisation of every
+// live expanded row, and the top-k weight folded into the fp32 scale.
+//
+// Sources: SGLang moe_runner/deep_gemm.py source, _run_contiguous_gemm
+// (SiLU*up between the two grouped GEMMs, then per-token-group fp8 quant
+// with 128-wide groups), _situ_mul_quant_contig_kernel (the quantisation
+// rule: amax clamped at 1e-10, codes y * (448 / amax), scale amax / 448),
+// _cast_to_e8m0_with_rounding_up (power-of-two scales rounded up); SGLang
+// PR 37261 Modifications/Core (fold the row's top-k weight into the down
+// projection's fp32 input scale; not under UE8M0).
+//
+// One wave per row (grid-stride over rows up to the device-side total).
+// Each lane handles 8 columns per 512-column chunk; the 16 lanes of a
+// 128-column group reduce their max with xor-shuffles.  HBM-bound: reads the
+// bf16 gate/up row once, writes fp8 codes and one scale per group.
+#include "common.hpp"
+
+namespace moe {
+namespace {
+
+constexpr int kThreads = 256;
+constexpr int kRowsPerBlock = kThreads / 64;
+
+__device__ __forceinline__ float silu_mul(float g, float u) {
+  const float den = __fadd_rn(1.0f, expf(-g));
+  return __fmul_rn(__fdiv_rn(g, den), u);
+}
+
+__device__ __forceinline__ uint32_t e8m0_round_up(float s) {
+  const uint32_t bits = __float_as_uint(s);
+  const uint32_t ex = bits >> 23, mant = bits & 0x7fffffu;
+  const bool bump = (mant > 0) && (ex != 0xfe) && !(ex == 0 && mant <= 0x400000u);
+  return ex + (bump ? 1u : 0u);
+}
+
+template <bool kUe8m0, bool kFold>
+__global__ __launch_bounds__(kThreads) void act_quant_kernel(
+    const uint16_t* __restrict__ gu, const int32_t* __restrict__ m_indices,
+    const int32_t* __restrict__ psum, const int32_t* __restrict__ status, int64_t capacity,
+    int inter, int E, const float* __restrict__ fold_w, uint8_t* __restrict__ out,
+    uint8_t* __restrict__ out_scale) {
+  const int lane = threadIdx.x & 63;
+  const int64_t nrows = min((int64_t)status[0], capacity);
+  const int ngroups = inter / kGroup;
+  const int sbytes = kUe8m0 ? 1 : 4;
+  for (int64_t m = (int64_t)blockIdx.x * kRowsPerBlock + (threadIdx.x >> 6); m < nrows;
+       m += (int64_t)gridDim.x * kRowsPerBlock) {
+    const int e = m_indices[m];
+    if (e < 0 || e >= E) continue;
+    uint8_t* qrow = out + m * inter;
+    uint8_t* srow = out_scale + m * ngroups * sbytes;
+    if (m >= psum[e]) {  // alignment pad row: zeros, G is not read
+      for (int c = lane; c < inter / 16; c += 64)
+        reinterpret_cast<uint4*>(qrow)[c] = make_uint4(0, 0, 0, 0);
+      for (int c = lane; c < ngroups * sbytes; c += 64) srow[c] = 0;
+      continue;
+    }
+    const float w = kFold ? fold_w[m] : 1.f;
+    const uint16_t* grow = gu + m * (int64_t)(2 * inter);
+    for (int c0 = 0; c0 < inter; c0 += 512) {
+      const int col = c0 + lane * 8;
+      const bool active = col < inter;
+      float y[8];
+      float amax = 0.f;
+      if (active) {
+        const uint4 gv = *reinterpret_cast<const uint4*>(grow + col);
+        const uint4 uv = *reinterpret_cast<const uint4*>(grow + inter + col);
+        const uint32_t ga[4] = {gv.x, gv.y, gv.z, gv.w};
+        const uint32_t ua[4] = {uv.x, uv.y, uv.z, uv.w};
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          y[2 * i] = silu_mul(__uint_as_float(ga[i] << 16), __uint_as_float(ua[i] << 16));
+          y[2 * i + 1] =
+              silu_mul(__uint_as_float(ga[i] & 0xffff0000u), __uint_as_float(ua[i] & 0xffff0000u));
+        }
+#pragma unroll
+        for (int i = 0; i < 8; ++i) amax = fmaxf(amax, fabsf(y[i]));
+      }
+#pragma unroll
+      for (int o = 8; o > 0; o >>= 1) amax = fmaxf(amax, __shfl_xor(amax, o, 64));
+      amax = fmaxf(amax, 1e-10f);
+      if (!active) continue;
+      float scale_out;
+      uint32_t sbyte = 0;
+      float p[8];
+      if (kUe8m0) {
+        sbyte = e8m0_round_up(__fdiv_rn(amax, 448.0f));
+#pragma unroll
+        for (int i = 0; i < 8; ++i) p[i] = ldexpf(y[i], 127 - (int)sbyte);
+      } else {
+        const float inv = __fdiv_rn(448.0f, amax);
+        scale_out = __fdiv_rn(amax, 448.0f);
+        if (kFold) scale_out = __fmul_rn(scale_out, w);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) p[i] = __fmul_rn(y[i], inv);
+      }
+      int lo = __builtin_amdgcn_cvt_pk_fp8_f32(p[0], p[1], 0, false);
+      lo = __builtin_amdgcn_cvt_pk_fp8_f32(p[2], p[3], lo, true);
+      int hi = __builtin_amdgcn_cvt_pk_fp8_f32(p[4], p[5], 0, false);
+      hi = __builtin_amdgcn_cvt_pk_fp8_f32(p[6], p[7], hi, true);
+      *reinterpret_cast<uint2*>(qrow + col) = make_uint2((uint32_t)lo, (uint32_t)hi);
+      if ((lane & 15) == 0) {
+        const int grp = col / kGroup;
+        if (kUe8m0) srow[grp] = (uint8_t)sbyte;
+        else reinterpret_cast<float*>(srow)[grp] = scale_out;
+      }
+    }
+  }
+}
+
+}  // namespace
+}  // namespace moe
+
+using namespace moe;
+
+extern "C" moe_status moe_act_quant(const void* gate_up, const int32_t* m_indices,
+                                    const int32_t* psum, const int32_t* status, int64_t capacity,
+                                    int inter, int num_experts, int align, moe_scale_fmt fmt,
+                                    const float* fold_weight, void* out, void* out_scale,
+                                    void* stream) {
+  if (capacity < 0 || capacity > (1LL << 30) || inter <= 0 || inter % kGroup != 0 ||
+      num_experts < 1 || num_experts > MOE_MAX_EXPERTS)
+    return MOE_ERR_SHAPE;
+  if (align < MOE_MIN_ALIGN || align > MOE_MAX_ALIGN || (align & (align - 1)))
+    return MOE_ERR_UNSUPPORTED;
+  if (capacity % align != 0) return MOE_ERR_SHAPE;
+  if (fmt != MOE_SCALE_F32 && fmt != MOE_SCALE_UE8M0) return MOE_ERR_UNSUPPORTED;
+  if (fmt == MOE_SCALE_UE8M0 && fold_weight) return MOE_ERR_UNSUPPORTED;
+  if (!m_indices || !psum || !status) return MOE_ERR_NULL;
+  if (capacity > 0 && (!gate_up || !out || !out_scale)) return MOE_ERR_NULL;
+  if (((uintptr_t)gate_up % 16) || ((uintptr_t)out % 16)) return MOE_ERR_ALIGNMENT;
+  if (capacity == 0) return MOE_OK;
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  int64_t grid = (capacity + kRowsPerBlock - 1) / kRowsPerBlock;
+  if (grid > 4096) grid = 4096;
+  auto kern = fmt == MOE_SCALE_UE8M0 ? act_quant_kernel<true, false>
+              : fold_weight           ? act_quant_kernel<false, true>
+                                      : act_quant_kernel<false, false>;
+  hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(kThreads), 0, s, (const uint16_t*)gate_up,
+                     m_indices, psum, status, capacity, inter, num_experts, fold_weight,
+                     (uint8_t*)out, (uint8_t*)out_scale);
+  if (hipGetLastError() != hipSuccess) return MOE_ERR_LAUNCH;
+  return MOE_OK;
+}

@@ -1,0 +1,61 @@
+// Shared device helpers for the gfx950 kernels of libmoe_expand.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "moe_expand.h"
+
+namespace moe {
+
+constexpr int kWave = 64;
+constexpr int kGroup = 128;  // quantisation group / block edge
+
+__device__ __forceinline__ int64_t valid_rows(const int32_t* psum_recv_per_rank,
+                                              int num_src_ranks, int64_t rows) {
+  if (psum_recv_per_rank == nullptr || num_src_ranks <= 0) return rows;
+  int64_t v = psum_recv_per_rank[num_src_ranks - 1];
+  return v < 0 ? 0 : (v > rows ? rows : v);
+}
+
+__device__ __forceinline__ int align_up_i(int x, int a) { return (x + a - 1) & ~(a - 1); }
+
+// Wave-wide reductions and scans over 64 lanes (ds_swizzle/bpermute based).
+__device__ __forceinline__ int wave_min_i(int v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v = min(v, __shfl_xor(v, o, kWave));
+  return v;
+}
+__device__ __forceinline__ int wave_sum_i(int v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, kWave);
+  return v;
+}
+__device__ __forceinline__ int wave_or_i(int v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v |= __shfl_xor(v, o, kWave);
+  return v;
+}
+// Inclusive prefix sum over lanes.
+__device__ __forceinline__ int wave_incl_scan_i(int v) {
+  const int lane = threadIdx.x & (kWave - 1);
+#pragma unroll
+  for (int o = 1; o < kWave; o <<= 1) {
+    int t = __shfl_up(v, o, kWave);
+    if (lane >= o) v += t;
+  }
+  return v;
+}
+
+// fp32 -> bf16 bits, round to nearest even (NaN stays a quiet NaN).
+__device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return (uint16_t)((u >> 16) | 0x40);
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return (uint16_t)(u >> 16);
+}
+__device__ __forceinline__ float bf16_to_f32(uint16_t h) {
+  return __uint_as_float(((uint32_t)h) << 16);
+}
+
+}  // namespace moe

@@ -1,0 +1,390 @@
+// moe_expand_layout: received fp8 tokens -> per-(token, expert) rows grouped
+// by expert, each expert block padded to `align` rows, with row labels, the
+// slot->row map and the expand-mode prefix sum.  No host synchronisation.
+//
+// Sources: SGLang PR 37261 "expanded (do_expand=True) prefill dispatch for
+// DeepEP-V2" (Modifications/Core: row labels from the device psum; review
+// thread: psum[e] = align(psum[e-1]) + count[e], total = align(psum[E-1]));
+// vLLM PR 54109 PaddedStandard (Motivation/Design: -1 slots, device-side
+// real/padding boundary, zeroed alignment gaps).
+//
+// Three kernels on one stream:
+//  1. count   one thread per row; per-32-row-group expert counts (LDS
+//             atomics, order-free) -> workspace.
+//  2. scan    one workgroup: per-expert exclusive scan over the groups
+//             (one wave per expert column), then the expert starts as the
+//             exclusive scan of the aligned counts (start[e] is the sum of
+//             align(count) over e' < e, because every start is aligned),
+//             psum, total and flags.
+//  3. scatter one workgroup per 32-row group.  Wave 0 ranks the group's
+//             slots in ascending (row, k) order per expert (wave min over
+//             the experts present, then a lane prefix sum of per-row
+//             counts), giving src2dst; then all four waves copy each source
+//             row once to every destination with 16-byte loads/stores.
+//             The same grid zero-fills the alignment pad rows and writes the
+//             row labels (grid-stride), so no extra pass is needed.
+#include "common.hpp"
+
+namespace moe {
+namespace {
+
+constexpr int kGroupRows = 32;     // rows ranked together (one wave)
+constexpr int kCountThreads = 256; // rows per count workgroup
+constexpr int kGroupsPerCount = kCountThreads / kGroupRows;
+constexpr int kScanThreads = 1024;
+constexpr int kScatterThreads = 256;
+
+struct Workspace {
+  int32_t* grp;       // [ngroups][E]: counts, then exclusive offsets
+  int32_t* grp_flag;  // [ngroups]
+  int32_t* starts;    // [E]
+  int32_t* padbase;   // [E + 1] exclusive prefix of pad rows per expert
+};
+
+__host__ __device__ inline int64_t num_groups(int64_t rows) {
+  return (rows + kGroupRows - 1) / kGroupRows;
+}
+
+__host__ __device__ inline size_t round256(size_t b) { return (b + 255) & ~size_t(255); }
+
+__host__ __device__ inline size_t workspace_bytes(int64_t rows, int E) {
+  int64_t ng = num_groups(rows);
+  return round256(size_t(ng) * E * 4) + round256(size_t(ng) * 4) + round256(size_t(E) * 4) +
+         round256(size_t(E + 1) * 4);
+}
+
+__host__ __device__ inline Workspace carve(void* base, int64_t rows, int E) {
+  int64_t ng = num_groups(rows);
+  char* p = (char*)base;
+  Workspace w;
+  w.grp = (int32_t*)p;
+  p += round256(size_t(ng) * E * 4);
+  w.grp_flag = (int32_t*)p;
+  p += round256(size_t(ng) * 4);
+  w.starts = (int32_t*)p;
+  p += round256(size_t(E) * 4);
+  w.padbase = (int32_t*)p;
+  return w;
+}
+
+__global__ __launch_bounds__(kCountThreads) void expand_count_kernel(
+    const int32_t* __restrict__ ids, const int32_t* __restrict__ psum_rank, int nsrc,
+    int64_t rows, int topk, int E, int64_t ngroups, int32_t* __restrict__ grp,
+    int32_t* __restrict__ grp_flag) {
+  extern __shared__ int32_t lds_cnt[];  // [kGroupsPerCount][E] then flags
+  int32_t* lflag = lds_cnt + kGroupsPerCount * E;
+  const int t = threadIdx.x;
+  for (int i = t; i < kGroupsPerCount * E; i += kCountThreads) lds_cnt[i] = 0;
+  if (t < kGroupsPerCount) lflag[t] = 0;
+  __syncthreads();
+  const int64_t nv = valid_rows(psum_rank, nsrc, rows);
+  const int64_t r = (int64_t)blockIdx.x * kCountThreads + t;
+  const int g = t / kGroupRows;
+  if (r < nv) {
+    int bad = 0;
+    const int32_t* row = ids + r * topk;
+    for (int k = 0; k < topk; ++k) {
+      int e = row[k];
+      if (e >= E) bad = 1;
+      else if (e >= 0) atomicAdd(&lds_cnt[g * E + e], 1);
+    }
+    if (bad) atomicOr(&lflag[g], MOE_FLAG_EXPERT_ID_RANGE);
+  }
+  __syncthreads();
+  const int64_t g0 = (int64_t)blockIdx.x * kGroupsPerCount;
+  for (int i = t; i < kGroupsPerCount * E; i += kCountThreads) {
+    int64_t gg = g0 + i / E;
+    if (gg < ngroups) grp[gg * E + (i % E)] = lds_cnt[i];
+  }
+  if (t < kGroupsPerCount && g0 + t < ngroups) grp_flag[g0 + t] = lflag[t];
+}
+
+// Exclusive scan over the whole 1024-thread workgroup; returns the exclusive
+// prefix of v and writes the total to *total (all threads).
+__device__ int block_excl_scan(int v, int* lds16, int* total) {
+  const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
+  int incl = wave_incl_scan_i(v);
+  if (lane == 63) lds16[wid] = incl;
+  __syncthreads();
+  int wsum = (lane < kScanThreads / 64) ? lds16[lane] : 0;
+  int wincl = wave_incl_scan_i(wsum);
+  int wbase = __shfl(wincl - wsum, wid, 64);
+  *total = __shfl(wincl, kScanThreads / 64 - 1, 64);
+  __syncthreads();
+  return wbase + incl - v;
+}
+
+__global__ __launch_bounds__(kScanThreads) void expand_scan_kernel(
+    int32_t* __restrict__ grp, const int32_t* __restrict__ grp_flag, int64_t ngroups, int E,
+    int align, int64_t capacity, int32_t* __restrict__ starts, int32_t* __restrict__ padbase,
+    int32_t* __restrict__ psum, int32_t* __restrict__ status) {
+  __shared__ int lds_count[MOE_MAX_EXPERTS];
+  __shared__ int lds16[16];
+  __shared__ int lds_flag;
+  const int t = threadIdx.x, lane = t & 63, wid = t >> 6;
+  if (t == 0) lds_flag = 0;
+  __syncthreads();
+  // Column scans: wave `wid` owns experts wid, wid+16, ...; lane l owns a
+  // contiguous run of groups so the order of groups is preserved.
+  const int64_t per = (ngroups + 63) / 64;
+  for (int e = wid; e < E; e += kScanThreads / 64) {
+    int64_t lo = lane * per, hi = min(lo + per, ngroups);
+    int s = 0;
+    for (int64_t g = lo; g < hi; ++g) s += grp[g * E + e];
+    int incl = wave_incl_scan_i(s);
+    int run = incl - s;
+    for (int64_t g = lo; g < hi; ++g) {
+      int c = grp[g * E + e];
+      grp[g * E + e] = run;
+      run += c;
+    }
+    if (lane == 63) lds_count[e] = incl;
+  }
+  int f = 0;
+  for (int64_t g = t; g < ngroups; g += kScanThreads) f |= grp_flag[g];
+  if (f) atomicOr(&lds_flag, f);
+  __syncthreads();
+  const int cnt = t < E ? lds_count[t] : 0;
+  const int blk = align_up_i(cnt, align);
+  int total;
+  const int start = block_excl_scan(blk, lds16, &total);
+  int padtot;
+  const int pb = block_excl_scan(blk - cnt, lds16, &padtot);
+  if (t < E) {
+    starts[t] = start;
+    psum[t] = start + cnt;
+    padbase[t] = pb;
+  }
+  if (t == 0) {
+    padbase[E] = padtot;
+    status[0] = total;
+    status[1] = lds_flag | (total > capacity ? MOE_FLAG_CAPACITY_OVERFLOW : 0);
+  }
+}
+
+// Largest index i in [0, n) with a[i] <= v (a non-decreasing, a[0] <= v).
+__device__ __forceinline__ int last_le(const int32_t* a, int n, int v) {
+  int lo = 0, hi = n - 1;
+  while (lo < hi) {
+    int mid = (lo + hi + 1) >> 1;
+    if (a[mid] <= v) lo = mid;
+    else hi = mid - 1;
+  }
+  return lo;
+}
+
+__global__ __launch_bounds__(kScatterThreads) void expand_scatter_kernel(
+    const uint8_t* __restrict__ x, int64_t x_stride, const uint8_t* __restrict__ x_scale,
+    int64_t x_scale_stride_bytes, int scale_bytes, const int32_t* __restrict__ ids,
+    const float* __restrict__ topk_w, const int32_t* __restrict__ psum_rank, int nsrc,
+    int64_t rows, int hidden, int topk, int E, int64_t capacity,
+    const int32_t* __restrict__ grp_off, const int32_t* __restrict__ starts_g,
+    const int32_t* __restrict__ padbase_g, const int32_t* __restrict__ psum_g,
+    const int32_t* __restrict__ status, uint8_t* __restrict__ ex, uint8_t* __restrict__ ex_scale,
+    int32_t* __restrict__ m_indices, int32_t* __restrict__ src2dst, float* __restrict__ row_weight) {
+  extern __shared__ int32_t lds[];
+  int32_t* l_starts = lds;                       // [E]
+  int32_t* l_padbase = l_starts + E;             // [E + 1]
+  int32_t* l_ids = l_padbase + E + 1;            // [kGroupRows][topk]
+  int32_t* l_dst = l_ids + kGroupRows * topk;    // [kGroupRows][topk]
+  int32_t* l_live = l_dst + kGroupRows * topk;   // [kGroupRows]
+  const int t = threadIdx.x, lane = t & 63, wid = t >> 6;
+  const int64_t g = blockIdx.x;
+  const int64_t nv = valid_rows(psum_rank, nsrc, rows);
+  const int total = status[0];
+  const int64_t nrows_ex = min((int64_t)total, capacity);
+
+  for (int i = t; i < E; i += kScatterThreads) l_starts[i] = starts_g[i];
+  for (int i = t; i <= E; i += kScatterThreads) l_padbase[i] = padbase_g[i];
+  const int64_t r0 = g * kGroupRows;
+  if (g < num_groups(rows)) {
+    for (int i = t; i < kGroupRows * topk; i += kScatterThreads) {
+      int64_t r = r0 + i / topk;
+      l_ids[i] = (r < nv) ? ids[r0 * topk + i] : -1;
+      l_dst[i] = -1;
+    }
+  }
+  __syncthreads();
+
+  if (g < num_groups(rows)) {
+    // ---- rank (wave 0): stable order (row, k) within each expert ----
+    if (wid == 0) {
+      const bool valid = lane < kGroupRows && r0 + lane < nv;
+      const int32_t* my = l_ids + (lane < kGroupRows ? lane : 0) * topk;
+      int32_t* myd = l_dst + (lane < kGroupRows ? lane : 0) * topk;
+      int last = -1, nlive = 0;
+      for (;;) {
+        int mine = 0x7fffffff;
+        if (valid)
+          for (int k = 0; k < topk; ++k) {
+            int e = my[k];
+            if (e > last && e < E && e < mine) mine = e;
+          }
+        const int emin = wave_min_i(mine);
+        if (emin == 0x7fffffff) break;
+        int c = 0;
+        if (valid)
+          for (int k = 0; k < topk; ++k) c += (my[k] == emin);
+        const int pre = wave_incl_scan_i(c) - c;
+        const int base = l_starts[emin] + grp_off[g * E + emin];
+        if (c) {
+          int j = 0;
+          for (int k = 0; k < topk; ++k) {
+            if (my[k] == emin) {
+              int64_t d = (int64_t)base + pre + j++;
+              if (d < capacity) {
+                myd[k] = (int)d;
+                ++nlive;
+                if (row_weight) row_weight[d] = topk_w[(r0 + lane) * topk + k];
+              }
+            }
+          }
+        }
+        last = emin;
+      }
+      if (lane < kGroupRows) l_live[lane] = nlive;
+    }
+    __syncthreads();
+    // src2dst for every row of the group (rows >= R_v get -1 everywhere)
+    for (int i = t; i < kGroupRows * topk; i += kScatterThreads) {
+      int64_t r = r0 + i / topk;
+      if (r < rows) src2dst[r0 * topk + i] = l_dst[i];
+    }
+    // ---- copy: one wave per source row, 16-byte chunks, read once ----
+    const int nch = hidden / 16;
+    for (int i = wid; i < kGroupRows; i += kScatterThreads / 64) {
+      if (l_live[i] == 0) continue;
+      const int64_t r = r0 + i;
+      const uint4* src = reinterpret_cast<const uint4*>(x + r * x_stride);
+      const int32_t* dl = l_dst + i * topk;
+      for (int c0 = 0; c0 < nch; c0 += 64 * 4) {
+        uint4 v[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          int c = c0 + u * 64 + lane;
+          if (c < nch) v[u] = src[c];
+        }
+        for (int k = 0; k < topk; ++k) {
+          const int d = dl[k];
+          if (d < 0) continue;
+          uint4* dst = reinterpret_cast<uint4*>(ex + (int64_t)d * hidden);
+#pragma unroll
+          for (int u = 0; u < 4; ++u) {
+            int c = c0 + u * 64 + lane;
+            if (c < nch) dst[c] = v[u];
+          }
+        }
+      }
+      const int nsc = hidden / kGroup;
+      for (int c = lane; c < nsc; c += 64) {
+        if (scale_bytes == 4) {
+          const float s = reinterpret_cast<const float*>(x_scale + r * x_scale_stride_bytes)[c];
+          for (int k = 0; k < topk; ++k) {
+            const int d = dl[k];
+            if (d >= 0) reinterpret_cast<float*>(ex_scale + (int64_t)d * nsc * 4)[c] = s;
+          }
+        } else {
+          const uint8_t s = (x_scale + r * x_scale_stride_bytes)[c];
+          for (int k = 0; k < topk; ++k) {
+            const int d = dl[k];
+            if (d >= 0) (ex_scale + (int64_t)d * nsc)[c] = s;
+          }
+        }
+      }
+    }
+  }
+
+  // ---- grid-stride: alignment pad rows and row labels ----
+  const int64_t gthreads = (int64_t)gridDim.x * kScatterThreads;
+  const int64_t gtid = (int64_t)blockIdx.x * kScatterThreads + t;
+  for (int64_t i = gtid; i < capacity; i += gthreads) {
+    int lab = -1;
+    if (i < nrows_ex) lab = last_le(l_starts, E, (int)i);
+    m_indices[i] = lab;
+  }
+  const int npad = l_padbase[E];
+  const int64_t gwaves = (int64_t)gridDim.x * (kScatterThreads / 64);
+  const int nsc = hidden / kGroup;
+  for (int64_t p = (int64_t)blockIdx.x * (kScatterThreads / 64) + wid; p < npad; p += gwaves) {
+    const int e = last_le(l_padbase, E, (int)p);
+    const int64_t row = (int64_t)psum_g[e] + (p - l_padbase[e]);
+    if (row >= capacity) continue;
+    uint4* dst = reinterpret_cast<uint4*>(ex + row * hidden);
+    const uint4 z = make_uint4(0, 0, 0, 0);
+    for (int c = lane; c < hidden / 16; c += 64) dst[c] = z;
+    for (int c = lane; c < nsc * scale_bytes; c += 64) ex_scale[row * nsc * scale_bytes + c] = 0;
+    if (lane == 0 && row_weight) row_weight[row] = 0.f;
+  }
+}
+
+}  // namespace
+}  // namespace moe
+
+using namespace moe;
+
+extern "C" size_t moe_expand_workspace_bytes(int64_t rows, int topk, int num_experts) {
+  if (rows < 0 || topk < 1 || topk > MOE_MAX_TOPK || num_experts < 1 ||
+      num_experts > MOE_MAX_EXPERTS)
+    return 0;
+  return workspace_bytes(rows, num_experts);
+}
+
+extern "C" moe_status moe_expand_layout(
+    const void* x, int64_t x_stride, const void* x_scale, int64_t x_scale_stride,
+    moe_scale_fmt fmt, const int32_t* topk_ids, const float* topk_weights,
+    const int32_t* psum_recv_per_rank, int num_src_ranks, int64_t rows, int hidden, int topk,
+    int num_experts, int align, int64_t capacity, void* ex, void* ex_scale, int32_t* psum,
+    int32_t* m_indices, int32_t* src2dst, float* row_weight, int32_t* status, void* workspace,
+    size_t workspace_bytes_, void* stream) {
+  if (rows < 0 || hidden <= 0 || hidden % kGroup != 0 || topk < 1 || topk > MOE_MAX_TOPK ||
+      num_experts < 1 || num_experts > MOE_MAX_EXPERTS || capacity < 0 || rows > (1LL << 30) ||
+      capacity > (1LL << 30) || (int64_t)rows * topk > (1LL << 30))
+    return MOE_ERR_SHAPE;
+  if (align < MOE_MIN_ALIGN || align > MOE_MAX_ALIGN || (align & (align - 1)))
+    return MOE_ERR_UNSUPPORTED;
+  if (capacity % align != 0) return MOE_ERR_SHAPE;
+  if (fmt != MOE_SCALE_F32 && fmt != MOE_SCALE_UE8M0) return MOE_ERR_UNSUPPORTED;
+  if (x_stride < hidden || x_scale_stride < hidden / kGroup) return MOE_ERR_SHAPE;
+  if (num_src_ranks < 0 || (psum_recv_per_rank && num_src_ranks == 0)) return MOE_ERR_SHAPE;
+  if (!psum || !m_indices || !src2dst || !status) return MOE_ERR_NULL;
+  if (rows > 0 && (!x || !x_scale || !topk_ids)) return MOE_ERR_NULL;
+  if (capacity > 0 && (!ex || !ex_scale)) return MOE_ERR_NULL;
+  if (row_weight && !topk_weights && rows > 0) return MOE_ERR_NULL;
+  if ((x_stride % 16) || ((uintptr_t)x % 16) || ((uintptr_t)ex % 16)) return MOE_ERR_ALIGNMENT;
+  if (!workspace || workspace_bytes_ < workspace_bytes(rows, num_experts))
+    return MOE_ERR_WORKSPACE;
+  if ((uintptr_t)workspace % 256) return MOE_ERR_ALIGNMENT;
+
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  const int E = num_experts;
+  const int64_t ng = num_groups(rows);
+  Workspace w = carve(workspace, rows, E);
+  const int scale_bytes = fmt == MOE_SCALE_F32 ? 4 : 1;
+
+  if (ng > 0) {
+    const int64_t nblk = (rows + kCountThreads - 1) / kCountThreads;
+    size_t lds = size_t(kGroupsPerCount) * E * 4 + kGroupsPerCount * 4;
+    hipLaunchKernelGGL(expand_count_kernel, dim3((unsigned)nblk), dim3(kCountThreads), lds, s,
+                       topk_ids, psum_recv_per_rank, num_src_ranks, rows, topk, E, ng, w.grp,
+                       w.grp_flag);
+    if (hipGetLastError() != hipSuccess) return MOE_ERR_LAUNCH;
+  }
+  hipLaunchKernelGGL(expand_scan_kernel, dim3(1), dim3(kScanThreads), 0, s, w.grp, w.grp_flag, ng,
+                     E, align, capacity, w.starts, w.padbase, psum, status);
+  if (hipGetLastError() != hipSuccess) return MOE_ERR_LAUNCH;
+
+  // Enough workgroups to cover the row groups, and at least a few hundred so
+  // the label fill and pad zeroing spread over the chip.
+  int64_t grid = ng;
+  const int64_t min_grid = 512;
+  if (grid < min_grid) grid = min_grid;
+  size_t lds = size_t(E) * 4 + size_t(E + 1) * 4 + size_t(kGroupRows) * topk * 8 + kGroupRows * 4;
+  hipLaunchKernelGGL(expand_scatter_kernel, dim3((unsigned)grid), dim3(kScatterThreads), lds, s,
+                     (const uint8_t*)x, x_stride, (const uint8_t*)x_scale,
+                     x_scale_stride * scale_bytes, scale_bytes, topk_ids, topk_weights,
+                     psum_recv_per_rank, num_src_ranks, rows, hidden, topk, E, capacity, w.grp,
+                     w.starts, w.padbase, psum, status, (uint8_t*)ex, (uint8_t*)ex_scale,
+                     m_indices, src2dst, row_weight);
+  if (hipGetLastError() != hipSuccess) return MOE_ERR_LAUNCH;
+  return MOE_OK;
+}

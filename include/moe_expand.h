@@ -1,0 +1,237 @@
+/*
+ * moe_expand.h -- C ABI of libmoe_expand.so: one expert-parallel rank's MoE
+ * expert computation on the expanded dispatch layout, for AMD Instinct
+ * MI355X (gfx950).
+ *
+ * The path, in call order (all on one HIP stream, no host synchronisation,
+ * no host read of device data):
+ *
+ *   moe_expand_layout     received fp8 tokens + top-k ids/weights
+ *                          -> per-(token, expert) rows grouped by expert,
+ *                             each expert block padded to `align` rows,
+ *                             row->expert labels, slot->row map, psum
+ *   moe_grouped_gemm_fp8  gate_up projection (w13), bf16 out
+ *   moe_act_quant         SiLU(gate)*up, per-1x128 fp8 quantisation, and
+ *                          (fp32 scales) the top-k weight folded into the
+ *                          down projection's input scale
+ *   moe_grouped_gemm_fp8  down projection (w2), bf16 out
+ *   moe_gather            each token's expert rows summed back into one
+ *                          bf16 row (weighted here under UE8M0 scales)
+ *
+ * Sources, by page and section:
+ *  [P1] SGLang pull request 37261, "feat(deepep_v2): expanded (do_expand=True)
+ *       prefill dispatch for DeepEP-V2": Modifications/Core (row labels from
+ *       the device psum with no cumsum, host copy or sentinel; the weight
+ *       fold into down_proj's fp32 input scale and the UE8M0 fallback), the
+ *       SGLANG_DEEPEP_V2_PREFILL_DO_EXPAND section (expanded rows grouped by
+ *       expert), and the review thread's note on the expand-mode psum
+ *       (psum[e] = align(psum[e-1]) + count[e]; total rows = align(psum[E-1])).
+ *  [P2] vLLM pull request 54109, PaddedStandard activation format:
+ *       Motivation (inactive rows carry -1 in every top-k slot; the real /
+ *       padding boundary psum_recv_per_rank lives on the device; prefill
+ *       alignment gaps are zeroed) and Design (the kernel must skip inactive
+ *       rows or make them safe to discard, and honour -1 markers rather than
+ *       trust row contents).
+ *  [P3] SGLang moe_runner/deep_gemm.py source page: _run_contiguous_gemm
+ *       (gate_up GEMM, SiLU*up, per-token-group fp8 quant, down GEMM),
+ *       _get_compact_all_tokens (capacity bound), _cast_to_e8m0_with_
+ *       rounding_up (UE8M0 rule), pre_permute_deepep_v2_to_deep_gemm and
+ *       post_permute_deep_gemm_to_deepep_v2 (expanded branch).
+ *
+ * Conventions for every call:
+ *  - Pointers named as device buffers are device memory the caller owns
+ *    (allocated, e.g., by PyTorch).  The library never allocates, frees,
+ *    copies between host and device, synchronises, or reads device data on
+ *    the host.  `stream` is a hipStream_t (NULL = the default stream); work
+ *    is enqueued asynchronously on it.
+ *  - Host-detectable errors (null pointers, bad sizes, misaligned buffers,
+ *    unsupported combinations) are returned as a moe_status before anything
+ *    is launched, and nothing is written.  MOE_ERR_LAUNCH reports a failed
+ *    kernel launch.
+ *  - Device-detected conditions are OR-ed into status[1] by
+ *    moe_expand_layout (MOE_FLAG_*); later calls clamp to what is valid.
+ *  - fp8 is OCP E4M3 ("fn": bias 7, max 448, no infinities).  bf16 buffers
+ *    hold raw 16-bit patterns.  fp32 scales are IEEE float; UE8M0 scales are
+ *    one unsigned exponent byte per group, value 2^(b-127).
+ *  - Activation scales are row-major [rows, K/128] (one per 1x128 group);
+ *    weight scales are [E, N/128, K/128] (one per 128x128 block).
+ *  - Calls are stateless and reentrant; calls that share output buffers
+ *    must be ordered by the caller's streams.
+ */
+#ifndef MOE_EXPAND_H
+#define MOE_EXPAND_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  MOE_OK = 0,
+  MOE_ERR_NULL = 1,         /* a required pointer is NULL                 */
+  MOE_ERR_SHAPE = 2,        /* a size is out of range or inconsistent     */
+  MOE_ERR_ALIGNMENT = 3,    /* a pointer or stride is not 16-byte aligned */
+  MOE_ERR_UNSUPPORTED = 4,  /* valid in principle, not supported          */
+  MOE_ERR_WORKSPACE = 5,    /* workspace missing or too small             */
+  MOE_ERR_LAUNCH = 6        /* a kernel launch failed                     */
+} moe_status;
+
+typedef enum {
+  MOE_SCALE_F32 = 0,        /* fp32 scale per group                       */
+  MOE_SCALE_UE8M0 = 1       /* one power-of-two exponent byte per group   */
+} moe_scale_fmt;
+
+/* Bits of status[1] written by moe_expand_layout. */
+#define MOE_FLAG_CAPACITY_OVERFLOW 1 /* total rows > capacity: rows at or past
+                                        the capacity were dropped (their slots
+                                        get -1)                               */
+#define MOE_FLAG_EXPERT_ID_RANGE 2   /* a valid row held an id >= num_experts;
+                                        that slot was skipped                 */
+
+/* Limits of this build. */
+#define MOE_MAX_EXPERTS 1024
+#define MOE_MAX_TOPK 32
+#define MOE_MIN_ALIGN 16
+#define MOE_MAX_ALIGN 1024
+
+/* Text for a moe_status value (static storage; never NULL). */
+const char* moe_status_string(int status);
+
+/* Host, pure.  Largest padded row total over every routing of rows*topk
+ * assignments onto num_experts experts with blocks rounded up to `align`
+ * rows: align * (n + (rows*topk - n) / align), n = min(rows*topk, E)
+ * [P3 _get_compact_all_tokens].  Use it to size the expanded buffers
+ * without reading the device-side row count.  Returns -1 on bad input. */
+int64_t moe_expand_capacity(int64_t rows, int topk, int num_experts, int align);
+
+/* Host, pure.  Bytes of device workspace moe_expand_layout needs for
+ * `rows` receive-buffer rows.  Returns 0 on bad input. */
+size_t moe_expand_workspace_bytes(int64_t rows, int topk, int num_experts);
+
+/*
+ * Expanded layout [P1 Core + psum note; P2 Motivation/Design; P3
+ * pre_permute_deepep_v2_to_deep_gemm].
+ *
+ * Inputs (device):
+ *   x              [rows, x_stride] bytes, fp8 token rows (hidden bytes used)
+ *   x_scale        [rows, x_scale_stride] fp32 or UE8M0 bytes (by fmt)
+ *   topk_ids       [rows, topk] int32; id < 0 = not for this rank / inactive;
+ *                  id >= num_experts is skipped and flagged
+ *   topk_weights   [rows, topk] fp32; may be NULL only if row_weight is NULL
+ *   psum_recv_per_rank [num_src_ranks] int32 inclusive prefix sum of rows
+ *                  received per source rank; its last entry is the number of
+ *                  valid rows R_v (clamped to [0, rows]).  NULL: R_v = rows.
+ *                  Rows >= R_v are never read as routing.
+ * Sizes: hidden % 128 == 0; 1 <= topk <= MOE_MAX_TOPK; 1 <= num_experts <=
+ *   MOE_MAX_EXPERTS; align a power of two in [16, 1024]; capacity a multiple
+ *   of align (moe_expand_capacity gives one that cannot overflow);
+ *   x_stride % 16 == 0 and x 16-byte aligned.
+ * Outputs (device, caller-allocated):
+ *   ex             [capacity, hidden] fp8 expanded rows
+ *   ex_scale       [capacity, hidden/128] scales (same format as x_scale)
+ *   psum           [num_experts] int32, psum[e] = align(psum[e-1]) + count[e]
+ *   m_indices      [capacity] int32: expert of each expanded row, alignment
+ *                  pads included; -1 from the total to the capacity
+ *   src2dst        [rows, topk] int32: expanded row of each live slot, -1
+ *                  otherwise (all slots of rows >= R_v are -1)
+ *   row_weight     [capacity] fp32 top-k weight of each expanded row (0 on
+ *                  pads); may be NULL
+ *   status         [2] int32: status[0] = total expanded rows
+ *                  align(psum[E-1]) (may exceed capacity: see the flag),
+ *                  status[1] = MOE_FLAG_* bits
+ * Rows of one expert are in ascending (row, k) order.  Alignment pad rows
+ * get fp8 zero, scale 0 and weight 0.  Rows from the total up to the
+ * capacity are left untouched.
+ * workspace: device, >= moe_expand_workspace_bytes(rows, topk, num_experts)
+ *   bytes, 256-byte aligned, no initialisation needed.
+ */
+moe_status moe_expand_layout(
+    const void* x, int64_t x_stride, const void* x_scale,
+    int64_t x_scale_stride, moe_scale_fmt fmt,
+    const int32_t* topk_ids, const float* topk_weights,
+    const int32_t* psum_recv_per_rank, int num_src_ranks,
+    int64_t rows, int hidden, int topk, int num_experts, int align,
+    int64_t capacity,
+    void* ex, void* ex_scale, int32_t* psum, int32_t* m_indices,
+    int32_t* src2dst, float* row_weight, int32_t* status,
+    void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Contiguous grouped fp8 GEMM, "NT": out[m, :] = A[m, :] . W[e]^T with
+ * e = m_indices[m] [P3 _run_contiguous_gemm; P1 Core].
+ *
+ *   a        [capacity, k] fp8 (row stride k), a_scale [capacity, k/128]
+ *   w        [num_experts, n, k] fp8 (k contiguous), w_scale
+ *            [num_experts, n/128, k/128]; a_scale and w_scale in `fmt`
+ *   m_indices, psum, status  as written by moe_expand_layout
+ *   out      [capacity, n] bf16
+ * Computes, for every row m < min(status[0], capacity) with 0 <= e < E:
+ *   out[m,j] = bf16( sum_kb sa[m,kb] * sw[e,j/128,kb] *
+ *                    sum_{t in kb} a[m,t] * w[e,j,t] )
+ * accumulated in fp32 (UE8M0: the exponents are applied by the matrix
+ * cores).  Row tiles made only of alignment padding (rows >= psum[e]) may be
+ * skipped and left unwritten; rows past the total are never written.
+ * Sizes: n % 128 == 0, k % 128 == 0, align as for the layout, capacity a
+ * multiple of align; a, w, out 16-byte aligned.
+ */
+moe_status moe_grouped_gemm_fp8(
+    const void* a, const void* a_scale, moe_scale_fmt fmt,
+    const void* w, const void* w_scale,
+    const int32_t* m_indices, const int32_t* psum, const int32_t* status,
+    int64_t capacity, int n, int k, int num_experts, int align,
+    void* out, void* stream);
+
+/*
+ * SiLU(gate)*up with per-1x128 fp8 quantisation [P3 _run_contiguous_gemm,
+ * _situ_mul_quant_contig_kernel (quantisation rule), _cast_to_e8m0_with_
+ * rounding_up; P1 Core (fold)].
+ *
+ *   gate_up   [capacity, 2*inter] bf16: gate = first half, up = second
+ *   m_indices, psum, status  as written by moe_expand_layout
+ *   fold_weight  [capacity] fp32 (the layout's row_weight) or NULL.  Only
+ *                with MOE_SCALE_F32 (UE8M0 + fold -> MOE_ERR_UNSUPPORTED).
+ *   out       [capacity, inter] fp8; out_scale [capacity, inter/128] in fmt
+ * For each live row m (m < min(status[0], capacity), m < psum[e]):
+ *   y = g / (1 + exp(-g)) * u in fp32; per group amax = max(|y|, 1e-10);
+ *   F32:   s = amax / 448, q = fp8_rne(y * (448 / amax)), s *= fold_weight[m]
+ *   UE8M0: b = smallest power-of-two exponent byte with 2^(b-127) >= amax/448,
+ *          q = fp8_rne(y * 2^(127-b))
+ * Alignment pad rows (psum[e] <= m < align(psum[e])) get q = 0, scale 0.
+ * Sizes: inter % 128 == 0; gate_up and out 16-byte aligned.
+ */
+moe_status moe_act_quant(
+    const void* gate_up, const int32_t* m_indices, const int32_t* psum,
+    const int32_t* status, int64_t capacity, int inter, int num_experts,
+    int align, moe_scale_fmt fmt, const float* fold_weight,
+    void* out, void* out_scale, void* stream);
+
+/*
+ * Weighted gather back to token rows [P3 post_permute_deep_gemm_to_deepep_v2
+ * and ep_gather's use in post_permute_deep_gemm_to_deepep_normal; P1 Core
+ * (UE8M0 weighting of the down output)].
+ *
+ *   expert_out   [capacity, hidden] bf16 (down projection output)
+ *   src2dst      [rows, topk] int32 as written by moe_expand_layout;
+ *                entries outside [0, capacity) are treated as -1
+ *   topk_weights [rows, topk] fp32, or NULL when the weights were folded
+ *   psum_recv_per_rank / num_src_ranks  as for the layout (R_v)
+ *   out          [rows, hidden] bf16
+ * For r < R_v: out[r] = bf16( sum over k ascending with src2dst[r,k] >= 0 of
+ *   c_k * float(expert_out[src2dst[r,k]]) ), c_k = topk_weights[r,k] or 1,
+ * each product and sum rounded to fp32 in that order.  Valid rows with no
+ * live slot become 0.  Rows >= R_v are not written.
+ * Sizes: hidden % 128 == 0; buffers 16-byte aligned.
+ */
+moe_status moe_gather(
+    const void* expert_out, const int32_t* src2dst, const float* topk_weights,
+    const int32_t* psum_recv_per_rank, int num_src_ranks,
+    int64_t rows, int hidden, int topk, int64_t capacity,
+    void* out, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MOE_EXPAND_H */

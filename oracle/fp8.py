@@ -43,41 +43,49 @@ def decode_e4m3(codes) -> np.ndarray:
     return E4M3_TABLE[np.asarray(codes, dtype=np.uint8)]
 
 
-def encode_e4m3(values) -> np.ndarray:
-    """Float values -> uint8 E4M3(fn) codes, round to nearest, ties to even.
+_POS = E4M3_TABLE[:0x7F]                     # codes 0x00..0x7E, increasing
+_MIDS = (_POS[:-1] + _POS[1:]) / 2.0          # exact in float64
 
-    Magnitudes that round above 448 become NaN (0x7F with the sign bit), as
-    does NaN and +-inf: the format has no infinity and this encoder does not
-    saturate.  -0.0 keeps its sign bit.
-    """
-    v = np.asarray(values, dtype=np.float64)
-    neg = np.signbit(v)
-    a = np.abs(v)
-    out = np.zeros(v.shape, dtype=np.uint8)
-    finite = np.isfinite(a)
-    a_f = np.where(finite, a, 0.0)
-    # Spacing of representable values around a: subnormal spacing 2^-9 below
-    # the smallest normal 2^-6, else 2^(floor(log2 a) - 3).
-    _, ex = np.frexp(a_f)                       # a = f * 2^ex, f in [0.5, 1)
-    e_unb = ex.astype(np.int64) - 1             # floor(log2 a) for a > 0
-    spacing_exp = np.where(a_f < 2.0 ** -6, -9, e_unb - 3)
-    q = np.rint(np.ldexp(a_f, -spacing_exp))    # exact scale; rint is RNE
-    qa = np.ldexp(q, spacing_exp)               # rounded magnitude (exact)
-    # Encode the rounded magnitude.
-    _, qex = np.frexp(qa)
-    qe = qex.astype(np.int64) - 1
-    normal = qa >= 2.0 ** -6
-    exp_field = np.where(normal, qe + 7, 0)
-    mant = np.where(normal,
-                    np.rint(np.ldexp(qa, -qe) * 8.0 - 8.0),
-                    np.rint(np.ldexp(qa, 9)))
-    overflow = qa > E4M3_MAX
-    code = (exp_field.astype(np.int64) << 3) | mant.astype(np.int64)
-    code = np.where(overflow | ~finite, E4M3_NAN, code)
-    code = np.where(np.isnan(v), E4M3_NAN, code)
-    out[...] = code.astype(np.uint8)
-    out |= np.where(neg, 0x80, 0).astype(np.uint8)
-    return out
+
+def encode_e4m3(values) -> np.ndarray:
+    """Float values -> uint8 E4M3(fn) codes: the nearest representable
+    magnitude, ties to the even code (even mantissa), sign kept.
+
+    Magnitudes above 464 (the midpoint between 448 and the NaN slot) become
+    NaN (0x7F with the sign bit), as do NaN and +-inf: the format has no
+    infinity and this encoder does not saturate.  -0.0 keeps its sign bit.
+
+    float32 input is rounded on its bit pattern (round to nearest even at
+    the third mantissa bit; subnormals as multiples of 2^-9); any other input
+    is converted to float64 and matched against the table of midpoints."""
+    v = np.asarray(values)
+    if v.dtype == np.float32:
+        a = np.abs(v)
+        code = _encode_f32_magnitude(a)
+    else:
+        v = v.astype(np.float64)
+        a = np.abs(v)
+        code = np.searchsorted(_MIDS, a, side="left")     # midpoints below a
+        tie = (code < len(_MIDS)) & (_MIDS[np.minimum(code, len(_MIDS) - 1)] == a)
+        code = np.where(tie & (code % 2 == 1), code + 1, code)
+    bad = ~(a <= 464.0)                                   # > 464, inf or NaN
+    code = np.where(bad, E4M3_NAN, code).astype(np.uint8)
+    return code | np.where(np.signbit(v), 0x80, 0).astype(np.uint8)
+
+
+def _encode_f32_magnitude(a):
+    """|v| as float32 -> E4M3 code (before the overflow check)."""
+    bits = np.ascontiguousarray(a).view(np.uint32)
+    # Normal range (>= 2^-6): round to nearest-even at the third mantissa bit;
+    # the top 12 bits are then (float32 exponent, 3 mantissa bits), a carry
+    # moving into the exponent.  Rebias the exponent from 127 to 7.
+    top = (bits + np.uint32(0x7FFFF) + ((bits >> np.uint32(20)) & np.uint32(1))) \
+        >> np.uint32(20)
+    normal = top.astype(np.int32) - ((127 - 7) << 3)
+    # Subnormal range: multiples of 2^-9, nearest-even (rint); 8 is 2^-6.
+    sub = np.rint(a * np.float32(512.0)).astype(np.int32)
+    code = np.where(a >= np.float32(2.0 ** -6), normal, sub)
+    return np.minimum(code, 0x7F)
 
 
 def round_bf16(values) -> np.ndarray:

@@ -174,12 +174,15 @@ def layer(inp, mode: str = "auto"):
     return lay
 
 
-def brute_force(inp, mode: str = "auto"):
+def brute_force(inp, mode: str = "auto", rows=None):
     """Per-token evaluation with no layout: for each valid row r and each
     slot k naming a local expert, run that expert's MLP on the token with
     the same roundings as the layered path (bf16 gate_up, fp32 SiLU*up,
     per-1x128 fp8 quantisation, optional weight fold, bf16 down), and sum
-    the slots in ascending k in fp32 before one bf16 rounding."""
+    the slots in ascending k in fp32 before one bf16 rounding.
+
+    rows: optional list of valid row indices to evaluate (default: all);
+    the result has one output row per entry, in that order."""
     fmt = inp["fmt"]
     if mode == "auto":
         mode = "fold" if fmt == "f32" else "post"
@@ -190,10 +193,22 @@ def brute_force(inp, mode: str = "auto"):
     E, two_i, H = w13_q.shape
     inter = two_i // 2
     nv = int(inp["num_valid"])
-    W13 = [quant.dequant_block(w13_q[e], w13_s[e], fmt) for e in range(E)]
-    W2 = [quant.dequant_block(w2_q[e], w2_s[e], fmt) for e in range(E)]
-    out = np.zeros((nv, H), dtype=np.float32)
-    for r in range(nv):
+    rows = list(range(nv)) if rows is None else [int(r) for r in rows]
+    assert all(0 <= r < nv for r in rows)
+    cache13, cache2 = {}, {}
+
+    def w13_of(e):
+        if e not in cache13:
+            cache13[e] = quant.dequant_block(w13_q[e], w13_s[e], fmt)
+        return cache13[e]
+
+    def w2_of(e):
+        if e not in cache2:
+            cache2[e] = quant.dequant_block(w2_q[e], w2_s[e], fmt)
+        return cache2[e]
+
+    out = np.zeros((len(rows), H), dtype=np.float32)
+    for i, r in enumerate(rows):
         xr = quant.dequant_rows(np.asarray(inp["x_q"])[r:r + 1],
                                 np.asarray(inp["x_s"])[r:r + 1], fmt)
         acc = np.zeros(H, dtype=np.float32)
@@ -201,15 +216,15 @@ def brute_force(inp, mode: str = "auto"):
             e = int(ids[r, k])
             if e < 0 or e >= E:
                 continue
-            g = fp8.round_bf16(xr @ W13[e].T)[0]
+            g = fp8.round_bf16(xr @ w13_of(e).T)[0]
             y = silu_mul(g[:inter], g[inter:])
             q, s = quant.quantize_rows(y[None, :], fmt)
             if mode == "fold":
                 s = (s * wts[r, k]).astype(np.float32)
             yq = quant.dequant_rows(q, s, fmt)
-            d = fp8.round_bf16(yq @ W2[e].T)[0]
+            d = fp8.round_bf16(yq @ w2_of(e).T)[0]
             if mode == "post":
                 d = (d * wts[r, k]).astype(np.float32)
             acc = (acc + d).astype(np.float32)
-        out[r] = fp8.round_bf16(acc)
+        out[i] = fp8.round_bf16(acc)
     return out

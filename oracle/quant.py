@@ -35,7 +35,9 @@ def _codes_and_scales(v32: np.ndarray, amax: np.ndarray, fmt: str):
         return q, s
     if fmt == "ue8m0":
         b = fp8.e8m0_round_up((amax / F8_MAX).astype(np.float32))
-        q = fp8.encode_e4m3(np.ldexp(v32.astype(np.float64), 127 - b.astype(np.int64)))
+        # Scaling by a power of two is exact in float32 down to 2^-126; any
+        # value that small is far below the smallest fp8 step and encodes to 0.
+        q = fp8.encode_e4m3(np.ldexp(v32, (127 - b.astype(np.int32))).astype(np.float32))
         return q, b
     raise ValueError(f"unknown scale format {fmt!r}")
 

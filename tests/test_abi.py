@@ -1,0 +1,147 @@
+"""C-ABI library checks that need no GPU.
+
+The library loads, exports every function include/moe_expand.h declares,
+its host helpers agree with the oracle's capacity bound, and every entry
+point rejects bad arguments with the documented status before launching
+anything (the pointers passed here are never dereferenced: each case fails
+a host-side check).
+"""
+
+import ctypes
+
+import pytest
+
+import expanded_dispatch_layout_amd as M
+from oracle import layout as olayout
+
+FAKE = 0x100000          # 16-byte aligned, never dereferenced
+MIS = FAKE + 4           # misaligned
+
+
+def test_library_exports_every_header_function():
+    names = M.header_functions()
+    assert set(names) >= {"moe_expand_layout", "moe_grouped_gemm_fp8", "moe_act_quant",
+                          "moe_gather", "moe_expand_capacity",
+                          "moe_expand_workspace_bytes", "moe_status_string"}
+    lib = M.lib()
+    for n in names:
+        assert hasattr(lib, n), n
+        assert n in M._SIGNATURES, n
+
+
+@pytest.mark.parametrize("rows,topk,E,align", [
+    (64, 2, 4, 64), (4096, 8, 8, 128), (16384, 8, 16, 128), (8192, 8, 8, 128),
+    (0, 8, 8, 128), (1, 1, 1, 16), (3, 2, 100, 16), (1000, 4, 7, 32)])
+def test_capacity_matches_oracle(rows, topk, E, align):
+    assert M.moe_expand_capacity(rows, topk, E, align) == olayout.capacity(rows, topk, E, align)
+
+
+def test_capacity_bad_input():
+    assert M.moe_expand_capacity(-1, 2, 4, 16) == -1
+    assert M.moe_expand_capacity(4, 0, 4, 16) == -1
+
+
+def test_workspace_bytes():
+    assert M.moe_expand_workspace_bytes(4096, 8, 8) > 0
+    assert M.moe_expand_workspace_bytes(16384, 8, 16) >= M.moe_expand_workspace_bytes(4096, 8, 8)
+    assert M.moe_expand_workspace_bytes(10, 8, 0) == 0
+    assert M.moe_expand_workspace_bytes(10, 99, 8) == 0
+
+
+def test_status_strings():
+    for c in range(7):
+        assert M.status_string(c)
+    assert M.status_string(99) == "unknown status"
+
+
+def _layout(**kw):
+    a = dict(x=FAKE, x_stride=256, x_scale=FAKE, x_scale_stride=2, fmt=0, ids=FAKE,
+             w=FAKE, prank=None, nsrc=0, rows=64, hidden=256, topk=2, E=4, align=64,
+             cap=320, ex=FAKE, exs=FAKE, psum=FAKE, mi=FAKE, s2d=FAKE, rw=FAKE, st=FAKE,
+             ws=FAKE, wsb=0, stream=None)
+    a.update(kw)
+    return M.lib().moe_expand_layout(
+        a["x"], a["x_stride"], a["x_scale"], a["x_scale_stride"], a["fmt"], a["ids"],
+        a["w"], a["prank"], a["nsrc"], a["rows"], a["hidden"], a["topk"], a["E"],
+        a["align"], a["cap"], a["ex"], a["exs"], a["psum"], a["mi"], a["s2d"], a["rw"],
+        a["st"], a["ws"], a["wsb"], a["stream"])
+
+
+def test_layout_rejects_bad_arguments():
+    assert _layout(hidden=100) == M.MOE_ERR_SHAPE
+    assert _layout(topk=0) == M.MOE_ERR_SHAPE
+    assert _layout(topk=33) == M.MOE_ERR_SHAPE
+    assert _layout(E=0) == M.MOE_ERR_SHAPE
+    assert _layout(E=2000) == M.MOE_ERR_SHAPE
+    assert _layout(align=48) == M.MOE_ERR_UNSUPPORTED
+    assert _layout(align=8) == M.MOE_ERR_UNSUPPORTED
+    assert _layout(cap=100) == M.MOE_ERR_SHAPE
+    assert _layout(fmt=7) == M.MOE_ERR_UNSUPPORTED
+    assert _layout(x_stride=128) == M.MOE_ERR_SHAPE
+    assert _layout(prank=FAKE, nsrc=0) == M.MOE_ERR_SHAPE
+    assert _layout(psum=None) == M.MOE_ERR_NULL
+    assert _layout(x=None) == M.MOE_ERR_NULL
+    assert _layout(w=None) == M.MOE_ERR_NULL          # row_weight needs weights
+    assert _layout(x=MIS) == M.MOE_ERR_ALIGNMENT
+    assert _layout(x_stride=264) == M.MOE_ERR_ALIGNMENT
+    assert _layout(ws=None) == M.MOE_ERR_WORKSPACE
+    assert _layout(wsb=16) == M.MOE_ERR_WORKSPACE     # everything else valid
+
+
+def test_gemm_rejects_bad_arguments():
+    f = M.lib().moe_grouped_gemm_fp8
+
+    def call(**kw):
+        a = dict(a=FAKE, as_=FAKE, fmt=0, w=FAKE, ws=FAKE, mi=FAKE, psum=FAKE, st=FAKE,
+                 cap=256, n=256, k=256, E=4, align=64, out=FAKE)
+        a.update(kw)
+        return f(a["a"], a["as_"], a["fmt"], a["w"], a["ws"], a["mi"], a["psum"], a["st"],
+                 a["cap"], a["n"], a["k"], a["E"], a["align"], a["out"], None)
+    assert call(n=100) == M.MOE_ERR_SHAPE
+    assert call(k=192) == M.MOE_ERR_SHAPE
+    assert call(cap=100) == M.MOE_ERR_SHAPE
+    assert call(align=24) == M.MOE_ERR_UNSUPPORTED
+    assert call(fmt=3) == M.MOE_ERR_UNSUPPORTED
+    assert call(mi=None) == M.MOE_ERR_NULL
+    assert call(a=MIS) == M.MOE_ERR_ALIGNMENT
+    assert call(cap=0) == M.MOE_OK                  # nothing to do, nothing launched
+
+
+def test_act_quant_rejects_bad_arguments():
+    f = M.lib().moe_act_quant
+
+    def call(**kw):
+        a = dict(gu=FAKE, mi=FAKE, psum=FAKE, st=FAKE, cap=256, inter=128, E=4, align=64,
+                 fmt=0, fw=None, out=FAKE, os=FAKE)
+        a.update(kw)
+        return f(a["gu"], a["mi"], a["psum"], a["st"], a["cap"], a["inter"], a["E"],
+                 a["align"], a["fmt"], a["fw"], a["out"], a["os"], None)
+    assert call(inter=100) == M.MOE_ERR_SHAPE
+    # the weight fold needs fp32 scales (a power-of-two scale cannot absorb it)
+    assert call(fmt=1, fw=FAKE) == M.MOE_ERR_UNSUPPORTED
+    assert call(out=None) == M.MOE_ERR_NULL
+    assert call(gu=MIS) == M.MOE_ERR_ALIGNMENT
+    assert call(cap=0) == M.MOE_OK
+
+
+def test_gather_rejects_bad_arguments():
+    f = M.lib().moe_gather
+
+    def call(**kw):
+        a = dict(eo=FAKE, s2d=FAKE, w=None, prank=None, nsrc=0, rows=64, hidden=256,
+                 topk=2, cap=320, out=FAKE)
+        a.update(kw)
+        return f(a["eo"], a["s2d"], a["w"], a["prank"], a["nsrc"], a["rows"], a["hidden"],
+                 a["topk"], a["cap"], a["out"], None)
+    assert call(hidden=100) == M.MOE_ERR_SHAPE
+    assert call(topk=40) == M.MOE_ERR_SHAPE
+    assert call(s2d=None) == M.MOE_ERR_NULL
+    assert call(out=MIS) == M.MOE_ERR_ALIGNMENT
+    assert call(rows=0) == M.MOE_OK
+
+
+def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
+    monkeypatch.setattr(M, "LIB_PATH", str(tmp_path / "missing.so"))
+    monkeypatch.setattr(M, "_lib", None)
+    with pytest.raises(ImportError):
+        M.lib()

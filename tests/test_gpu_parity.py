@@ -1,0 +1,219 @@
+"""GPU parity: the HIP path (through the C ABI) against the CPU oracle.
+
+Bars:
+* layout, labels, slot map, psum, status, scattered bytes and scales, the
+  gather in fold mode and with weights: bit-exact;
+* grouped GEMM (bf16 out): the oracle rounds a float64 sum once, the GPU an
+  fp32 sum, so an element may differ by one bf16 rounding: |diff| <= 2^-8
+  |oracle| (half an ulp each side) plus 1e-6 absolute;
+* activation quantisation: scales within 2 fp32 ulps (the GPU's expf may
+  differ from numpy's by an ulp), fp8 codes equal except rare neighbours at
+  rounding ties (< 0.1% of codes, never more than one step apart);
+* layer output (bf16): |gpu - oracle| <= 1e-2 + 2e-2 |oracle| elementwise,
+  and |gpu - oracle| <= 0.05 * rms(oracle) + one bf16 ulp, a bar scaled to
+  the output so that small outputs are not waved through by the absolute
+  term.
+"""
+
+import numpy as np
+import pytest
+
+torch = pytest.importorskip("torch")
+
+import expanded_dispatch_layout_amd as M  # noqa: E402
+from oracle import fp8, layer, layout  # noqa: E402
+from tests._inputs import make, to_gpu  # noqa: E402
+
+pytestmark = pytest.mark.gpu
+
+if not torch.cuda.is_available():
+    pytest.skip("needs a GPU", allow_module_level=True)
+
+SENT = 0x5A
+
+
+def bf16_np(t):
+    return t.float().cpu().numpy()
+
+
+def run_gpu(inp, stop=None):
+    """Run the layer on the GPU through ExpandedMoE; return the module and the
+    output (rows >= R_v hold the sentinel pattern)."""
+    g = to_gpu(inp)
+    R, T = inp["ids"].shape
+    mod = M.ExpandedMoE(R, T, g["w13"], g["w13_scale"], g["w2"], g["w2_scale"], inp["align"],
+                        inp["fmt"])
+    for buf in (mod.ex, mod.dq):
+        buf.fill_(SENT)
+    mod.gate_up.fill_(1.5)
+    mod.down.fill_(1.5)
+    out = torch.full((R, mod.H), 7.0, dtype=torch.bfloat16, device="cuda")
+    mod.layout(g["x"], g["x_scale"], g["ids"], g["w"], g["prank"])
+    if stop != "layout":
+        mod.experts()
+        mod.gather(g["w"], g["prank"], out)
+    torch.cuda.synchronize()
+    return mod, out, g
+
+
+SMALL = [
+    ("tiny", {}),
+    ("tiny", dict(fmt="ue8m0")),
+    ("tiny", dict(align=16, topk=3, seed=77)),
+    ("tiny", dict(align=32, seed=80)),
+    ("tiny", dict(rows=50, experts=3, global_experts=5, align=128, seed=78)),
+    ("tiny", dict(rows=300, hidden=384, inter=256, experts=6, global_experts=9, topk=4,
+                  align=16, seed=81)),
+    ("tiny", dict(rows=40, valid_rows=23, src_ranks=4, seed=79)),
+    ("tiny", dict(rows=40, valid_rows=23, src_ranks=4, tail_alias=True, seed=79)),
+    ("tiny", dict(rows=200, hidden=512, inter=384, experts=5, global_experts=5, topk=2,
+                  align=64, fmt="ue8m0", seed=82)),
+]
+IDS = [f"{n}-{'-'.join(f'{k}{v}' for k, v in o.items())}" for n, o in SMALL]
+
+
+def check_layout(mod, inp):
+    R, T = inp["ids"].shape
+    E = inp["w13_q"].shape[0]
+    nv = layout.num_valid_rows(R, inp["psum_recv_per_rank"])
+    cap = mod.capacity
+    ref = layout.expand(inp["ids"], inp["w"], inp["x_q"], inp["x_s"], nv, E, inp["align"], cap)
+    st = mod.status.cpu().numpy()
+    assert st[0] == ref["total"] and st[1] == ref["flags"]
+    assert np.array_equal(mod.psum.cpu().numpy(), ref["psum"])
+    assert np.array_equal(mod.m_indices.cpu().numpy(), ref["m_indices"])
+    assert np.array_equal(mod.src2dst.cpu().numpy(), ref["src2dst"])
+    n = min(ref["total"], cap)
+    ex = mod.ex.cpu().numpy()
+    assert np.array_equal(ex[:n], ref["ex"])
+    assert np.all(ex[n:] == SENT)                         # past the total: untouched
+    assert np.array_equal(mod.ex_scale.cpu().numpy()[:n].view(np.uint8),
+                          np.ascontiguousarray(ref["ex_scale"]).view(np.uint8))
+    assert np.array_equal(mod.row_weight.cpu().numpy()[:n].view(np.uint32),
+                          ref["row_weight"].view(np.uint32))
+    return ref
+
+
+@pytest.mark.parametrize("name,over", SMALL, ids=IDS)
+def test_layout_bit_exact(name, over):
+    inp = make(name, **over)
+    mod, _, _ = run_gpu(inp, stop="layout")
+    check_layout(mod, inp)
+
+
+def test_layout_flags_and_bad_ids():
+    inp = make("tiny", seed=90)
+    inp["ids"] = inp["ids"].copy()
+    inp["ids"][3, 0] = 9          # >= E: skipped and flagged
+    inp["ids"][5, 1] = 4
+    mod, _, _ = run_gpu(inp, stop="layout")
+    ref = check_layout(mod, inp)
+    assert ref["flags"] & layout.FLAG_EXPERT_ID_RANGE
+
+
+def test_layout_duplicate_ids():
+    inp = make("tiny", seed=91)
+    ids = inp["ids"].copy()
+    ids[:, 1] = np.where(ids[:, 0] >= 0, ids[:, 0], ids[:, 1])   # same expert twice
+    inp["ids"] = ids
+    mod, _, _ = run_gpu(inp, stop="layout")
+    check_layout(mod, inp)
+
+
+def _oracle_stage_inputs(inp):
+    return layer.layer({k: v for k, v in inp.items() if k not in ("psum_recv_per_rank",)}
+                       | {"num_valid": layout.num_valid_rows(len(inp["ids"]),
+                                                             inp["psum_recv_per_rank"])})
+
+
+def _bf16(a):
+    return torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).to(torch.bfloat16).cuda()
+
+
+@pytest.mark.parametrize("name,over", SMALL[:6] + SMALL[8:], ids=IDS[:6] + IDS[8:])
+def test_stages_against_oracle(name, over):
+    """Each stage fed the oracle's own inputs for that stage."""
+    inp = make(name, **over)
+    L = _oracle_stage_inputs(inp)
+    fmt, align = inp["fmt"], inp["align"]
+    g = to_gpu(inp)
+    R, T = inp["ids"].shape
+    mod = M.ExpandedMoE(R, T, g["w13"], g["w13_scale"], g["w2"], g["w2_scale"], align, fmt)
+    mod.layout(g["x"], g["x_scale"], g["ids"], g["w"], g["prank"])
+    n = min(L["total"], mod.capacity)
+    live = L["live"]
+    # GEMM1 on the oracle's expanded rows (identical bytes, checked above)
+    M.moe_grouped_gemm_fp8(mod.ex, mod.ex_scale, fmt, mod.w13, mod.w13_scale, mod.m_indices,
+                           mod.psum, mod.status, align, mod.gate_up)
+    torch.cuda.synchronize()
+    G = bf16_np(mod.gate_up)[:n]
+    ref = L["G"]
+    assert np.all(np.abs(G[live] - ref[live]) <= 2.0 ** -8 * np.abs(ref[live]) + 1e-6)
+    # act_quant on the oracle's G
+    gu = torch.zeros_like(mod.gate_up)
+    gu[:n] = _bf16(np.nan_to_num(ref, nan=0.0))
+    fold = mod.row_weight if fmt == "f32" else None
+    M.moe_act_quant(gu, mod.m_indices, mod.psum, mod.status, mod.E, align, fmt, fold, mod.dq,
+                    mod.ds)
+    torch.cuda.synchronize()
+    dq = mod.dq.cpu().numpy()[:n]
+    ds = mod.ds.cpu().numpy()[:n]
+    assert np.array_equal(dq[~live], L["dq"][~live]) and not ds[~live].any()
+    diff = dq[live] != L["dq"][live]
+    assert diff.mean() < 1e-3
+    step = np.abs(fp8.decode_e4m3(dq[live][diff]).astype(np.float64)
+                  - fp8.decode_e4m3(L["dq"][live][diff]))
+    mag = np.abs(fp8.decode_e4m3(L["dq"][live][diff]))
+    assert np.all(step <= np.maximum(mag, 2.0 ** -6) * 2.0 ** -3 + 2.0 ** -9)
+    if fmt == "f32":
+        assert np.allclose(ds[live], L["ds"][live], rtol=2.5e-7, atol=0)
+    else:
+        assert np.array_equal(ds[live], L["ds"][live])
+    # GEMM2 on the oracle's dq/ds
+    mod.dq[:n] = torch.from_numpy(L["dq"]).cuda()
+    mod.ds[:n] = torch.from_numpy(np.ascontiguousarray(L["ds"])).cuda()
+    M.moe_grouped_gemm_fp8(mod.dq, mod.ds, fmt, mod.w2, mod.w2_scale, mod.m_indices, mod.psum,
+                           mod.status, align, mod.down)
+    torch.cuda.synchronize()
+    D = bf16_np(mod.down)[:n]
+    assert np.all(np.abs(D[live] - L["D"][live]) <= 2.0 ** -8 * np.abs(L["D"][live]) + 1e-6)
+    # gather on the oracle's D: bit-exact
+    down = torch.zeros_like(mod.down)
+    down[:n] = _bf16(np.nan_to_num(L["D"], nan=0.0))
+    out = torch.full((R, mod.H), 3.0, dtype=torch.bfloat16, device="cuda")
+    wts = None if fmt == "f32" else g["w"]
+    M.moe_gather(down, mod.src2dst, wts, g["prank"], out)
+    torch.cuda.synchronize()
+    nv = L["out"].shape[0]
+    assert np.array_equal(bf16_np(out)[:nv], L["out"])
+
+
+def _check_output(got, ref):
+    err = np.abs(got - ref)
+    assert np.all(err <= 1e-2 + 2e-2 * np.abs(ref)), err.max()
+    rms = float(np.sqrt(np.mean(ref.astype(np.float64) ** 2)))
+    ulp = np.abs(ref) * 2.0 ** -8
+    assert np.all(err <= 0.05 * rms + ulp), (err.max(), rms)
+    return err.max(), rms
+
+
+@pytest.mark.parametrize("name,over", SMALL, ids=IDS)
+def test_layer_against_oracle(name, over):
+    inp = make(name, **over)
+    L = _oracle_stage_inputs(inp)
+    mod, out, _ = run_gpu(inp)
+    got = bf16_np(out)
+    nv = L["out"].shape[0]
+    emax, rms = _check_output(got[:nv], L["out"])
+    print(f"max|err| {emax:.3g}  rms(out) {rms:.3g}")
+    assert np.all(got[nv:] == 7.0)                        # rows past R_v untouched
+
+
+def test_layer_deterministic_and_tail_blind():
+    a = make("tiny", rows=40, valid_rows=23, src_ranks=4, seed=79)
+    b = make("tiny", rows=40, valid_rows=23, src_ranks=4, tail_alias=True, seed=79)
+    _, oa, _ = run_gpu(a)
+    _, oa2, _ = run_gpu(a)
+    _, ob, _ = run_gpu(b)
+    assert torch.equal(oa.view(torch.int16), oa2.view(torch.int16))
+    assert torch.equal(oa[:23].view(torch.int16), ob[:23].view(torch.int16))

@@ -68,6 +68,20 @@ def test_encode_random_matches_torch():
     assert np.array_equal(fp8.encode_e4m3(vals), torch_e4m3(vals))
 
 
+def test_encode_float64_path_agrees_and_rounds_once():
+    # Values exactly representable in float32 take the same code on both paths;
+    # values a hair above or below a midpoint (not float32 numbers) round once.
+    rng = np.random.default_rng(8)
+    v32 = (rng.uniform(-470, 470, 100000)).astype(np.float32)
+    assert np.array_equal(fp8.encode_e4m3(v32), fp8.encode_e4m3(v32.astype(np.float64)))
+    pos = np.sort(fp8.decode_e4m3(np.arange(0x00, 0x7F, dtype=np.uint8)))
+    mids = (pos[:-1] + pos[1:]) / 2.0
+    up = fp8.encode_e4m3(mids * (1 + 2.0 ** -40))
+    down = fp8.encode_e4m3(mids * (1 - 2.0 ** -40))
+    assert np.array_equal(up, np.arange(1, 0x7F, dtype=np.uint8))
+    assert np.array_equal(down[1:], np.arange(1, 0x7E, dtype=np.uint8))
+
+
 def test_encode_overflow_and_specials():
     # 464 is the tie between 448 and the NaN slot: ties to even gives 448;
     # anything above rounds past 448 and this non-saturating encoder gives NaN.
