@@ -3,16 +3,22 @@
 Bars:
 * layout, labels, slot map, psum, status, scattered bytes and scales, the
   gather in fold mode and with weights: bit-exact;
-* grouped GEMM (bf16 out): the oracle rounds a float64 sum once, the GPU an
-  fp32 sum, so an element may differ by one bf16 rounding: |diff| <= 2^-8
-  |oracle| (half an ulp each side) plus 1e-6 absolute;
+* grouped GEMM (bf16 out): the oracle rounds a float64 sum once; the GPU
+  sums in fp32 inside the matrix cores and rounds once.  Bound per element:
+  one bf16 ulp of the oracle value plus 2^-16 * sum_k |a_k w_k| (a generous
+  allowance for the fp32 accumulation, far below bf16 resolution for
+  ordinary values but not for results that cancel to near zero);
 * activation quantisation: scales within 2 fp32 ulps (the GPU's expf may
   differ from numpy's by an ulp), fp8 codes equal except rare neighbours at
   rounding ties (< 0.1% of codes, never more than one step apart);
-* layer output (bf16): |gpu - oracle| <= 1e-2 + 2e-2 |oracle| elementwise,
-  and |gpu - oracle| <= 0.05 * rms(oracle) + one bf16 ulp, a bar scaled to
-  the output so that small outputs are not waved through by the absolute
-  term.
+* layer output (bf16): |gpu - oracle| <= 1e-2 + 2e-2 |oracle| elementwise
+  (the stated bar), and, so that small outputs are not waved through by the
+  absolute term, rms(gpu - oracle) <= 1% of rms(oracle) and max|gpu -
+  oracle| <= 0.25 rms(oracle).  A one-ulp gate_up difference can move a
+  group's max and re-round all 128 fp8 codes of that group, so single
+  outputs can move by several percent of the rms; a wrong expert, sign,
+  weight or operand moves the rms error to order 100%.  (The pages' fp8 MoE
+  test scales its tolerance the same way: max error over output std.)
 """
 
 import numpy as np
@@ -34,6 +40,47 @@ SENT = 0x5A
 
 def bf16_np(t):
     return t.float().cpu().numpy()
+
+
+def ulp_diff(a, b):
+    """Distance in bf16 ulps between two arrays of bf16 values (as float32)."""
+    ia = (np.ascontiguousarray(a, np.float32).view(np.int32) >> 16).astype(np.int64)
+    ib = (np.ascontiguousarray(b, np.float32).view(np.int32) >> 16).astype(np.int64)
+    # map sign-magnitude to a monotone integer line
+    ia = np.where(ia < 0, -(ia & 0x7FFF), ia)
+    ib = np.where(ib < 0, -(ib & 0x7FFF), ib)
+    return np.abs(ia - ib)
+
+
+def bf16_ulp(ref):
+    a = np.abs(np.asarray(ref, np.float64))
+    e = np.floor(np.log2(np.maximum(a, 2.0 ** -126)))
+    return 2.0 ** (e - 7)
+
+
+def abs_terms(a_q, a_s, w_q, w_s, m_indices, rows, fmt):
+    """sum_k |a_mk w_nk| (dequantised) for the given rows: the scale of the
+    terms an fp32 accumulation error is proportional to."""
+    from oracle import quant
+    out = np.zeros((len(rows), w_q.shape[1]))
+    for e in np.unique(m_indices[rows]):
+        sel = np.nonzero(m_indices[rows] == e)[0]
+        A = np.abs(quant.dequant_rows(a_q[rows[sel]], a_s[rows[sel]], fmt))
+        Wd = np.abs(quant.dequant_block(w_q[e], w_s[e], fmt))
+        out[sel] = A @ Wd.T
+    return out
+
+
+def check_gemm(got, ref, terms, what):
+    diff = np.abs(got.astype(np.float64) - ref)
+    bound = bf16_ulp(ref) + 2.0 ** -16 * terms
+    frac = (diff > 0).mean()
+    worst = np.argsort((diff / bound).ravel())[-3:]
+    print(f"{what}: {frac:.4f} of elements differ, max diff/bound "
+          f"{(diff / bound).max():.3g}; worst (got, ref, terms): " +
+          ", ".join(f"({got.ravel()[i]:.6g}, {ref.ravel()[i]:.6g}, {terms.ravel()[i]:.3g})"
+                    for i in worst))
+    assert np.all(diff <= bound) and frac < 0.05
 
 
 def run_gpu(inp, stop=None):
@@ -148,7 +195,10 @@ def test_stages_against_oracle(name, over):
     torch.cuda.synchronize()
     G = bf16_np(mod.gate_up)[:n]
     ref = L["G"]
-    assert np.all(np.abs(G[live] - ref[live]) <= 2.0 ** -8 * np.abs(ref[live]) + 1e-6)
+    rows = np.nonzero(live)[0]
+    check_gemm(G[live], ref[live],
+               abs_terms(L["ex"], L["ex_scale"], inp["w13_q"], inp["w13_s"], L["m_indices"],
+                         rows, fmt), "gate_up")
     # act_quant on the oracle's G
     gu = torch.zeros_like(mod.gate_up)
     gu[:n] = _bf16(np.nan_to_num(ref, nan=0.0))
@@ -176,7 +226,9 @@ def test_stages_against_oracle(name, over):
                            mod.status, align, mod.down)
     torch.cuda.synchronize()
     D = bf16_np(mod.down)[:n]
-    assert np.all(np.abs(D[live] - L["D"][live]) <= 2.0 ** -8 * np.abs(L["D"][live]) + 1e-6)
+    check_gemm(D[live], L["D"][live],
+               abs_terms(L["dq"], L["ds"], inp["w2_q"], inp["w2_s"], L["m_indices"], rows, fmt),
+               "down")
     # gather on the oracle's D: bit-exact
     down = torch.zeros_like(mod.down)
     down[:n] = _bf16(np.nan_to_num(L["D"], nan=0.0))
@@ -189,11 +241,14 @@ def test_stages_against_oracle(name, over):
 
 
 def _check_output(got, ref):
-    err = np.abs(got - ref)
+    err = np.abs(got.astype(np.float64) - ref)
     assert np.all(err <= 1e-2 + 2e-2 * np.abs(ref)), err.max()
     rms = float(np.sqrt(np.mean(ref.astype(np.float64) ** 2)))
-    ulp = np.abs(ref) * 2.0 ** -8
-    assert np.all(err <= 0.05 * rms + ulp), (err.max(), rms)
+    erms = float(np.sqrt(np.mean(err ** 2)))
+    print(f"max|err| {err.max():.3g}  rms(err) {erms:.3g}  rms(out) {rms:.3g}  "
+          f"max/rms {err.max() / max(rms, 1e-30):.3g}  rms ratio {erms / max(rms, 1e-30):.3g}")
+    assert erms <= 0.01 * rms
+    assert err.max() <= 0.25 * rms
     return err.max(), rms
 
 
@@ -204,8 +259,7 @@ def test_layer_against_oracle(name, over):
     mod, out, _ = run_gpu(inp)
     got = bf16_np(out)
     nv = L["out"].shape[0]
-    emax, rms = _check_output(got[:nv], L["out"])
-    print(f"max|err| {emax:.3g}  rms(out) {rms:.3g}")
+    _check_output(got[:nv], L["out"])
     assert np.all(got[nv:] == 7.0)                        # rows past R_v untouched
 
 
