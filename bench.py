@@ -162,13 +162,13 @@ def main():
             mod.layout(inp["x"], inp["x_scale"], inp["ids"], inp["w"], inp["prank"])
         elif i == 1:
             M.moe_grouped_gemm_fp8(mod.ex, mod.ex_scale, wl.fmt, mod.w13, mod.w13_scale,
-                                   mod.m_indices, mod.psum, mod.status, wl.align, mod.gate_up)
+                                   mod.psum, mod.status, wl.align, mod.gate_up)
         elif i == 2:
             M.moe_act_quant(mod.gate_up, mod.m_indices, mod.psum, mod.status, mod.E, wl.align,
                             wl.fmt, fold, mod.dq, mod.ds)
         elif i == 3:
-            M.moe_grouped_gemm_fp8(mod.dq, mod.ds, wl.fmt, mod.w2, mod.w2_scale, mod.m_indices,
-                                   mod.psum, mod.status, wl.align, mod.down)
+            M.moe_grouped_gemm_fp8(mod.dq, mod.ds, wl.fmt, mod.w2, mod.w2_scale, mod.psum,
+                                   mod.status, wl.align, mod.down)
         else:
             mod.gather(inp["w"], inp["prank"], out)
 

@@ -39,7 +39,7 @@ _SIGNATURES = {
     "moe_expand_workspace_bytes": (_SZ, [_I64, _I, _I]),
     "moe_expand_layout": (_I, [_P, _I64, _P, _I64, _I, _P, _P, _P, _I, _I64, _I, _I,
                                _I, _I, _I64, _P, _P, _P, _P, _P, _P, _P, _P, _SZ, _P]),
-    "moe_grouped_gemm_fp8": (_I, [_P, _P, _I, _P, _P, _P, _P, _P, _I64, _I, _I, _I, _I,
+    "moe_grouped_gemm_fp8": (_I, [_P, _P, _I, _P, _P, _P, _P, _I64, _I, _I, _I, _I,
                                   _P, _P]),
     "moe_act_quant": (_I, [_P, _P, _P, _P, _I64, _I, _I, _I, _I, _P, _P, _P, _P]),
     "moe_gather": (_I, [_P, _P, _P, _P, _I, _I64, _I, _I, _I64, _P, _P]),
@@ -127,14 +127,14 @@ def moe_expand_layout(x, x_scale, fmt, topk_ids, topk_weights, psum_recv_per_ran
     _check("moe_expand_layout", code)
 
 
-def moe_grouped_gemm_fp8(a, a_scale, fmt, w, w_scale, m_indices, psum, status, align,
-                         out, stream=None):
+def moe_grouped_gemm_fp8(a, a_scale, fmt, w, w_scale, psum, status, align, out,
+                         stream=None):
     """a [capacity, k] fp8, w [E, n, k] fp8, out [capacity, n] bf16."""
     capacity, k = a.shape
     E, n, _ = w.shape
     code = lib().moe_grouped_gemm_fp8(
-        _ptr(a), _ptr(a_scale), _fmt(fmt), _ptr(w), _ptr(w_scale), _ptr(m_indices),
-        _ptr(psum), _ptr(status), capacity, n, k, E, align, _ptr(out), _stream(stream))
+        _ptr(a), _ptr(a_scale), _fmt(fmt), _ptr(w), _ptr(w_scale), _ptr(psum), _ptr(status),
+        capacity, n, k, E, align, _ptr(out), _stream(stream))
     _check("moe_grouped_gemm_fp8", code)
 
 
@@ -205,14 +205,12 @@ class ExpandedMoE:
 
     def experts(self, stream=None):
         moe_grouped_gemm_fp8(self.ex, self.ex_scale, self.fmt, self.w13, self.w13_scale,
-                             self.m_indices, self.psum, self.status, self.align,
-                             self.gate_up, stream)
+                             self.psum, self.status, self.align, self.gate_up, stream)
         fold = self.row_weight if self.fmt == "f32" else None
         moe_act_quant(self.gate_up, self.m_indices, self.psum, self.status, self.E,
                       self.align, self.fmt, fold, self.dq, self.ds, stream)
         moe_grouped_gemm_fp8(self.dq, self.ds, self.fmt, self.w2, self.w2_scale,
-                             self.m_indices, self.psum, self.status, self.align,
-                             self.down, stream)
+                             self.psum, self.status, self.align, self.down, stream)
 
     def gather(self, topk_weights, psum_recv_per_rank, out, stream=None):
         wts = None if self.fmt == "f32" else topk_weights

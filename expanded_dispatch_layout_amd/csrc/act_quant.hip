@@ -51,7 +51,7 @@ __global__ __launch_bounds__(kThreads) void act_quant_kernel(
     uint8_t* srow = out_scale + m * ngroups * sbytes;
     if (m >= psum[e]) {  // alignment pad row: zeros, G is not read
       for (int c = lane; c < inter / 16; c += 64)
-        reinterpret_cast<uint4*>(qrow)[c] = make_uint4(0, 0, 0, 0);
+        reinterpret_cast<u32x4*>(qrow)[c] = u32x4{0u, 0u, 0u, 0u};
       for (int c = lane; c < ngroups * sbytes; c += 64) srow[c] = 0;
       continue;
     }
@@ -63,10 +63,10 @@ __global__ __launch_bounds__(kThreads) void act_quant_kernel(
       float y[8];
       float amax = 0.f;
       if (active) {
-        const uint4 gv = *reinterpret_cast<const uint4*>(grow + col);
-        const uint4 uv = *reinterpret_cast<const uint4*>(grow + inter + col);
-        const uint32_t ga[4] = {gv.x, gv.y, gv.z, gv.w};
-        const uint32_t ua[4] = {uv.x, uv.y, uv.z, uv.w};
+        const u32x4 gv = *reinterpret_cast<const u32x4*>(grow + col);
+        const u32x4 uv = *reinterpret_cast<const u32x4*>(grow + inter + col);
+        const uint32_t ga[4] = {gv[0], gv[1], gv[2], gv[3]};
+        const uint32_t ua[4] = {uv[0], uv[1], uv[2], uv[3]};
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           y[2 * i] = silu_mul(__uint_as_float(ga[i] << 16), __uint_as_float(ua[i] << 16));

@@ -9,6 +9,10 @@
 namespace moe {
 
 constexpr int kWave = 64;
+
+// Native 16-byte vector.  HIP's uint4 is a class wrapping a union, and arrays
+// of it tend to be kept in scratch memory instead of registers.
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 constexpr int kGroup = 128;  // quantisation group / block edge
 
 __device__ __forceinline__ int64_t valid_rows(const int32_t* psum_recv_per_rank,

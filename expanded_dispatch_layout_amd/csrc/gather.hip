@@ -18,8 +18,8 @@ namespace {
 constexpr int kThreads = 256;
 constexpr int kRowsPerBlock = kThreads / 64;
 
-__device__ __forceinline__ void acc8(float* a, const uint4& v, float c, bool weighted) {
-  const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+__device__ __forceinline__ void acc8(float* a, const u32x4& v, float c, bool weighted) {
+  const uint32_t w[4] = {v[0], v[1], v[2], v[3]};
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     float lo = __uint_as_float(w[i] << 16);
@@ -65,29 +65,28 @@ __global__ __launch_bounds__(kThreads) void gather_kernel(
   const float* wt = l_w[wid];
   const bool weighted = topk_w != nullptr;
   const int nch = hidden / 8;  // 16-byte chunks of 8 bf16
-  uint4* orow = reinterpret_cast<uint4*>(out + r * hidden);
+  u32x4* orow = reinterpret_cast<u32x4*>(out + r * hidden);
   for (int c = lane; c < nch; c += 64) {
     float a[8];
 #pragma unroll
     for (int i = 0; i < 8; ++i) a[i] = 0.f;
     int k = 0;
     for (; k + 4 <= n; k += 4) {
-      uint4 v[4];
+      u32x4 v[4];
 #pragma unroll
       for (int u = 0; u < 4; ++u)
-        v[u] = reinterpret_cast<const uint4*>(eo + (int64_t)dst[k + u] * hidden)[c];
+        v[u] = reinterpret_cast<const u32x4*>(eo + (int64_t)dst[k + u] * hidden)[c];
 #pragma unroll
       for (int u = 0; u < 4; ++u) acc8(a, v[u], wt[k + u], weighted);
     }
     for (; k < n; ++k) {
-      uint4 v = reinterpret_cast<const uint4*>(eo + (int64_t)dst[k] * hidden)[c];
+      u32x4 v = reinterpret_cast<const u32x4*>(eo + (int64_t)dst[k] * hidden)[c];
       acc8(a, v, wt[k], weighted);
     }
-    uint4 o;
-    o.x = (uint32_t)f32_to_bf16_rne(a[0]) | ((uint32_t)f32_to_bf16_rne(a[1]) << 16);
-    o.y = (uint32_t)f32_to_bf16_rne(a[2]) | ((uint32_t)f32_to_bf16_rne(a[3]) << 16);
-    o.z = (uint32_t)f32_to_bf16_rne(a[4]) | ((uint32_t)f32_to_bf16_rne(a[5]) << 16);
-    o.w = (uint32_t)f32_to_bf16_rne(a[6]) | ((uint32_t)f32_to_bf16_rne(a[7]) << 16);
+    u32x4 o;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      o[i] = (uint32_t)f32_to_bf16_rne(a[2 * i]) | ((uint32_t)f32_to_bf16_rne(a[2 * i + 1]) << 16);
     orow[c] = o;
   }
 }

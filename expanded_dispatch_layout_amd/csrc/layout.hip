@@ -255,10 +255,10 @@ __global__ __launch_bounds__(kScatterThreads) void expand_scatter_kernel(
     for (int i = wid; i < kGroupRows; i += kScatterThreads / 64) {
       if (l_live[i] == 0) continue;
       const int64_t r = r0 + i;
-      const uint4* src = reinterpret_cast<const uint4*>(x + r * x_stride);
+      const u32x4* src = reinterpret_cast<const u32x4*>(x + r * x_stride);
       const int32_t* dl = l_dst + i * topk;
       for (int c0 = 0; c0 < nch; c0 += 64 * 4) {
-        uint4 v[4];
+        u32x4 v[4];
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
           int c = c0 + u * 64 + lane;
@@ -267,7 +267,7 @@ __global__ __launch_bounds__(kScatterThreads) void expand_scatter_kernel(
         for (int k = 0; k < topk; ++k) {
           const int d = dl[k];
           if (d < 0) continue;
-          uint4* dst = reinterpret_cast<uint4*>(ex + (int64_t)d * hidden);
+          u32x4* dst = reinterpret_cast<u32x4*>(ex + (int64_t)d * hidden);
 #pragma unroll
           for (int u = 0; u < 4; ++u) {
             int c = c0 + u * 64 + lane;
@@ -309,8 +309,8 @@ __global__ __launch_bounds__(kScatterThreads) void expand_scatter_kernel(
     const int e = last_le(l_padbase, E, (int)p);
     const int64_t row = (int64_t)psum_g[e] + (p - l_padbase[e]);
     if (row >= capacity) continue;
-    uint4* dst = reinterpret_cast<uint4*>(ex + row * hidden);
-    const uint4 z = make_uint4(0, 0, 0, 0);
+    u32x4* dst = reinterpret_cast<u32x4*>(ex + row * hidden);
+    const u32x4 z = {0u, 0u, 0u, 0u};
     for (int c = lane; c < hidden / 16; c += 64) dst[c] = z;
     for (int c = lane; c < nsc * scale_bytes; c += 64) ex_scale[row * nsc * scale_bytes + c] = 0;
     if (lane == 0 && row_weight) row_weight[row] = 0.f;

@@ -159,27 +159,30 @@ moe_status moe_expand_layout(
     void* workspace, size_t workspace_bytes, void* stream);
 
 /*
- * Contiguous grouped fp8 GEMM, "NT": out[m, :] = A[m, :] . W[e]^T with
- * e = m_indices[m] [P3 _run_contiguous_gemm; P1 Core].
+ * Contiguous grouped fp8 GEMM, "NT": out[m, :] = A[m, :] . W[e]^T for every
+ * expanded row m of expert e [P3 _run_contiguous_gemm; P1 Core].
  *
  *   a        [capacity, k] fp8 (row stride k), a_scale [capacity, k/128]
  *   w        [num_experts, n, k] fp8 (k contiguous), w_scale
  *            [num_experts, n/128, k/128]; a_scale and w_scale in `fmt`
- *   m_indices, psum, status  as written by moe_expand_layout
+ *   psum, status  as written by moe_expand_layout
  *   out      [capacity, n] bf16
- * Computes, for every row m < min(status[0], capacity) with 0 <= e < E:
+ * Expert e owns rows [align(psum[e-1]), align(psum[e])) -- exactly the rows
+ * moe_expand_layout labels e in m_indices -- so the kernel reads the layout
+ * from the device psum (no per-row labels needed).  For every such row
+ * m < min(status[0], capacity):
  *   out[m,j] = bf16( sum_kb sa[m,kb] * sw[e,j/128,kb] *
  *                    sum_{t in kb} a[m,t] * w[e,j,t] )
  * accumulated in fp32 (UE8M0: the exponents are applied by the matrix
- * cores).  Row tiles made only of alignment padding (rows >= psum[e]) may be
- * skipped and left unwritten; rows past the total are never written.
+ * cores).  Row groups made only of alignment padding (rows >= psum[e]) may
+ * be skipped and left unwritten; rows past the total are never written.
  * Sizes: n % 128 == 0, k % 128 == 0, align as for the layout, capacity a
- * multiple of align; a, w, out 16-byte aligned.
+ * multiple of align; a, w, out 16-byte aligned, scales 4-byte aligned.
  */
 moe_status moe_grouped_gemm_fp8(
     const void* a, const void* a_scale, moe_scale_fmt fmt,
     const void* w, const void* w_scale,
-    const int32_t* m_indices, const int32_t* psum, const int32_t* status,
+    const int32_t* psum, const int32_t* status,
     int64_t capacity, int n, int k, int num_experts, int align,
     void* out, void* stream);
 

@@ -92,17 +92,18 @@ def test_gemm_rejects_bad_arguments():
     f = M.lib().moe_grouped_gemm_fp8
 
     def call(**kw):
-        a = dict(a=FAKE, as_=FAKE, fmt=0, w=FAKE, ws=FAKE, mi=FAKE, psum=FAKE, st=FAKE,
+        a = dict(a=FAKE, as_=FAKE, fmt=0, w=FAKE, ws=FAKE, psum=FAKE, st=FAKE,
                  cap=256, n=256, k=256, E=4, align=64, out=FAKE)
         a.update(kw)
-        return f(a["a"], a["as_"], a["fmt"], a["w"], a["ws"], a["mi"], a["psum"], a["st"],
+        return f(a["a"], a["as_"], a["fmt"], a["w"], a["ws"], a["psum"], a["st"],
                  a["cap"], a["n"], a["k"], a["E"], a["align"], a["out"], None)
     assert call(n=100) == M.MOE_ERR_SHAPE
     assert call(k=192) == M.MOE_ERR_SHAPE
     assert call(cap=100) == M.MOE_ERR_SHAPE
     assert call(align=24) == M.MOE_ERR_UNSUPPORTED
     assert call(fmt=3) == M.MOE_ERR_UNSUPPORTED
-    assert call(mi=None) == M.MOE_ERR_NULL
+    assert call(psum=None) == M.MOE_ERR_NULL
+    assert call(as_=FAKE + 2) == M.MOE_ERR_ALIGNMENT
     assert call(a=MIS) == M.MOE_ERR_ALIGNMENT
     assert call(cap=0) == M.MOE_OK                  # nothing to do, nothing launched
 

@@ -190,8 +190,8 @@ def test_stages_against_oracle(name, over):
     n = min(L["total"], mod.capacity)
     live = L["live"]
     # GEMM1 on the oracle's expanded rows (identical bytes, checked above)
-    M.moe_grouped_gemm_fp8(mod.ex, mod.ex_scale, fmt, mod.w13, mod.w13_scale, mod.m_indices,
-                           mod.psum, mod.status, align, mod.gate_up)
+    M.moe_grouped_gemm_fp8(mod.ex, mod.ex_scale, fmt, mod.w13, mod.w13_scale, mod.psum,
+                           mod.status, align, mod.gate_up)
     torch.cuda.synchronize()
     G = bf16_np(mod.gate_up)[:n]
     ref = L["G"]
@@ -222,8 +222,8 @@ def test_stages_against_oracle(name, over):
     # GEMM2 on the oracle's dq/ds
     mod.dq[:n] = torch.from_numpy(L["dq"]).cuda()
     mod.ds[:n] = torch.from_numpy(np.ascontiguousarray(L["ds"])).cuda()
-    M.moe_grouped_gemm_fp8(mod.dq, mod.ds, fmt, mod.w2, mod.w2_scale, mod.m_indices, mod.psum,
-                           mod.status, align, mod.down)
+    M.moe_grouped_gemm_fp8(mod.dq, mod.ds, fmt, mod.w2, mod.w2_scale, mod.psum, mod.status,
+                           align, mod.down)
     torch.cuda.synchronize()
     D = bf16_np(mod.down)[:n]
     check_gemm(D[live], L["D"][live],
