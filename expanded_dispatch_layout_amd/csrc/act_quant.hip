@@ -9,17 +9,17 @@
 // PR 37261 Modifications/Core (fold the row's top-k weight into the down
 // projection's fp32 input scale; not under UE8M0).
 //
-// One wave per row (grid-stride over rows up to the device-side total).
-// Each lane handles 8 columns per 512-column chunk; the 16 lanes of a
-// 128-column group reduce their max with xor-shuffles.  HBM-bound: reads the
-// bf16 gate/up row once, writes fp8 codes and one scale per group.
+// One workgroup per row (grid-stride over rows up to the device-side total);
+// each thread handles 8 columns per 2048-column pass, so a whole I=2048 row is
+// one round trip; the 16 lanes of a 128-column group reduce their max with
+// xor-shuffles.  HBM-bound: reads the bf16 gate/up row once, writes fp8 codes
+// and one scale per group.
 #include "common.hpp"
 
 namespace moe {
 namespace {
 
-constexpr int kThreads = 256;
-constexpr int kRowsPerBlock = kThreads / 64;
+constexpr int kThreads = 256;  // one expanded row per workgroup
 
 __device__ __forceinline__ float silu_mul(float g, float u) {
   const float den = __fadd_rn(1.0f, expf(-g));
@@ -39,39 +39,38 @@ __global__ __launch_bounds__(kThreads) void act_quant_kernel(
     const int32_t* __restrict__ psum, const int32_t* __restrict__ status, int64_t capacity,
     int inter, int E, const float* __restrict__ fold_w, uint8_t* __restrict__ out,
     uint8_t* __restrict__ out_scale) {
-  const int lane = threadIdx.x & 63;
+  const int t = threadIdx.x, lane = t & 63;
   const int64_t nrows = min((int64_t)status[0], capacity);
   const int ngroups = inter / kGroup;
   const int sbytes = kUe8m0 ? 1 : 4;
-  for (int64_t m = (int64_t)blockIdx.x * kRowsPerBlock + (threadIdx.x >> 6); m < nrows;
-       m += (int64_t)gridDim.x * kRowsPerBlock) {
+  for (int64_t m = blockIdx.x; m < nrows; m += gridDim.x) {
     const int e = m_indices[m];
-    if (e < 0 || e >= E) continue;
+    if (e < 0 || e >= E) continue;  // uniform per workgroup
     uint8_t* qrow = out + m * inter;
     uint8_t* srow = out_scale + m * ngroups * sbytes;
     if (m >= psum[e]) {  // alignment pad row: zeros, G is not read
-      for (int c = lane; c < inter / 16; c += 64)
+      for (int c = t; c < inter / 16; c += kThreads)
         reinterpret_cast<u32x4*>(qrow)[c] = u32x4{0u, 0u, 0u, 0u};
-      for (int c = lane; c < ngroups * sbytes; c += 64) srow[c] = 0;
+      for (int c = t; c < ngroups * sbytes; c += kThreads) srow[c] = 0;
       continue;
     }
     const float w = kFold ? fold_w[m] : 1.f;
     const uint16_t* grow = gu + m * (int64_t)(2 * inter);
-    for (int c0 = 0; c0 < inter; c0 += 512) {
-      const int col = c0 + lane * 8;
+    // Each thread owns 8 consecutive columns per pass of kThreads*8 columns;
+    // the 16 threads of a 128-column group are 16 consecutive lanes.
+    for (int c0 = 0; c0 < inter; c0 += kThreads * 8) {
+      const int col = c0 + t * 8;
       const bool active = col < inter;
       float y[8];
       float amax = 0.f;
       if (active) {
         const u32x4 gv = *reinterpret_cast<const u32x4*>(grow + col);
         const u32x4 uv = *reinterpret_cast<const u32x4*>(grow + inter + col);
-        const uint32_t ga[4] = {gv[0], gv[1], gv[2], gv[3]};
-        const uint32_t ua[4] = {uv[0], uv[1], uv[2], uv[3]};
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          y[2 * i] = silu_mul(__uint_as_float(ga[i] << 16), __uint_as_float(ua[i] << 16));
+          y[2 * i] = silu_mul(__uint_as_float(gv[i] << 16), __uint_as_float(uv[i] << 16));
           y[2 * i + 1] =
-              silu_mul(__uint_as_float(ga[i] & 0xffff0000u), __uint_as_float(ua[i] & 0xffff0000u));
+              silu_mul(__uint_as_float(gv[i] & 0xffff0000u), __uint_as_float(uv[i] & 0xffff0000u));
         }
 #pragma unroll
         for (int i = 0; i < 8; ++i) amax = fmaxf(amax, fabsf(y[i]));
@@ -80,7 +79,7 @@ __global__ __launch_bounds__(kThreads) void act_quant_kernel(
       for (int o = 8; o > 0; o >>= 1) amax = fmaxf(amax, __shfl_xor(amax, o, 64));
       amax = fmaxf(amax, 1e-10f);
       if (!active) continue;
-      float scale_out;
+      float scale_out = 0.f;
       uint32_t sbyte = 0;
       float p[8];
       if (kUe8m0) {
@@ -131,8 +130,7 @@ extern "C" moe_status moe_act_quant(const void* gate_up, const int32_t* m_indice
   if (((uintptr_t)gate_up % 16) || ((uintptr_t)out % 16)) return MOE_ERR_ALIGNMENT;
   if (capacity == 0) return MOE_OK;
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
-  int64_t grid = (capacity + kRowsPerBlock - 1) / kRowsPerBlock;
-  if (grid > 4096) grid = 4096;
+  int64_t grid = capacity < 2048 ? capacity : 2048;  // grid-stride over the live rows
   auto kern = fmt == MOE_SCALE_UE8M0 ? act_quant_kernel<true, false>
               : fold_weight           ? act_quant_kernel<false, true>
                                       : act_quant_kernel<false, false>;

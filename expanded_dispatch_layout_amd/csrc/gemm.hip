@@ -22,8 +22,9 @@
 //  - Operands go HBM -> LDS directly (global_load_lds_dwordx4), three LDS
 //    stages, two K steps in flight; each wave waits only for its own oldest
 //    stage (explicit vmcnt) and a bare s_barrier publishes it.  The 16-byte
-//    chunks of every 128-byte row are XOR-swizzled by row, chosen per lane on
-//    the global side, so the 16-row fragment reads are bank-conflict free.
+//    chunks of every 128-byte row are XOR-swizzled by row (swz), chosen per
+//    lane on the global side, so the 16-row fragment reads are bank-conflict
+//    free.
 //  - fp32 scales: each step's MFMA result is promoted into the fp32
 //    accumulator with the row's activation scale times the block's weight
 //    scale (the scales do not factor out of the K sum).
@@ -62,8 +63,17 @@ constexpr int LOADS_PER_STAGE = A_LOADS + B_LOADS + 1;  // + one scale dword
 static_assert(GM * BN * 2 <= LDS_BYTES, "output tile must fit in LDS");
 static_assert(kWaves * 64 == 2 * GM, "scale loads: waves 0-3 A rows, 4-7 block scale");
 
+// Physical 16-byte chunk of logical chunk c in row r of a [rows][128 B] tile:
+// c ^ key(r), key(r) = (r & 7) ^ ((r >> 3) & 1).  A fragment read serves 16
+// consecutive rows (an aligned 16) at one logical chunk.  The key is a
+// permutation of the 8 chunks over any aligned 8 rows (conflict-free when 8
+// lanes are served per cycle over 32 banks), and over the 8 even (odd) rows
+// of an aligned 16 (conflict-free when 16 lanes are served over 64 banks,
+// where rows r and r+8 share banks).  It depends only on r mod 16, so every
+// fragment of a wave is one per-lane base plus a compile-time offset.
+__device__ __forceinline__ int swz_key(int row) { return (row & 7) ^ ((row >> 3) & 1); }
 __device__ __forceinline__ int swz(int row, int chunk) {  // byte offset in a [rows][128] tile
-  return row * 128 + ((chunk ^ (row & 7)) << 4);
+  return row * 128 + ((chunk ^ swz_key(row)) << 4);
 }
 
 __device__ __forceinline__ uint32_t lds_addr(const void* p) {
@@ -73,14 +83,16 @@ __device__ __forceinline__ uint32_t lds_addr(const void* p) {
 
 // Direct HBM -> LDS loads.  Issued from inline assembly so the compiler does
 // not treat them as LDS writes that every later LDS read must wait for: the
-// kernel orders them itself (vmcnt waits + s_barrier).  Lane i's data lands
-// at lds + i * size.
-__device__ __forceinline__ void dma16(const uint8_t* g, uint32_t lds) {
-  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(g), "s"(lds)
+// kernel orders them itself (vmcnt waits + s_barrier).  Address = 64-bit
+// scalar base + 32-bit per-lane offset; lane i's data lands at lds + i * size.
+__device__ __forceinline__ void dma16(const uint8_t* base, uint32_t off, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(off), "s"(base),
+               "s"(lds)
                : "memory");
 }
-__device__ __forceinline__ void dma4(const uint8_t* g, uint32_t lds) {
-  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dword %0, off" ::"v"(g), "s"(lds)
+__device__ __forceinline__ void dma4(const uint8_t* base, uint32_t off, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dword %0, %1" ::"v"(off), "s"(base),
+               "s"(lds)
                : "memory");
 }
 
@@ -90,6 +102,21 @@ __device__ __forceinline__ void wait_vmcnt() {
   asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
 }
 __device__ __forceinline__ void barrier() { asm volatile("s_barrier" ::: "memory"); }
+
+// Wait until at most n of this wave's vector-memory operations are
+// outstanding (n is wave-uniform; s_waitcnt takes an immediate).
+__device__ __forceinline__ void wait_vmcnt_rt(int n) {
+  switch (n) {
+    case 0: wait_vmcnt<0>(); break;
+    case 1: wait_vmcnt<1>(); break;
+    case 2: wait_vmcnt<2>(); break;
+    case 3: wait_vmcnt<3>(); break;
+    case 4: wait_vmcnt<4>(); break;
+    case 5: wait_vmcnt<5>(); break;
+    case 6: wait_vmcnt<6>(); break;
+    default: wait_vmcnt<LOADS_PER_STAGE>(); break;
+  }
+}
 
 struct Item {
   const uint8_t* a;     // first row of the group
@@ -105,48 +132,90 @@ struct Item {
   int sbytes;           // 4 (fp32) or 1 (UE8M0)
 };
 
-// Issue the direct-to-LDS loads of K step kb into `stage`.  Every wave issues
-// exactly LOADS_PER_STAGE instructions (rows past the live rows reload the
-// last live row) so the vmcnt bookkeeping is the same for all waves.
-__device__ __forceinline__ void issue_stage(const Item& it, uint8_t* stage, int kb, int lane,
-                                            int wid) {
+// Per-lane byte offsets of one item's loads, fixed over its K steps.
+struct LoadOffsets {
+  uint32_t a[A_LOADS];  // from it.a (+ kb * BK)
+  uint32_t b[B_LOADS];  // from it.b (+ kb * BK)
+  int scale_row;        // activation row whose scale this lane loads
+};
+
+__device__ __forceinline__ LoadOffsets load_offsets(const Item& it, int lane, int wid) {
+  LoadOffsets o;
+#pragma unroll
+  for (int j = 0; j < A_LOADS; ++j) {
+    const int r = (wid * A_LOADS + j) * 8 + (lane >> 3);
+    const int c = (lane & 7) ^ swz_key(r);
+    const int rr = r < it.live ? r : it.live - 1;  // reload the last live row
+    o.a[j] = (uint32_t)rr * (uint32_t)it.K + (uint32_t)c * 16u;
+  }
+#pragma unroll
+  for (int j = 0; j < B_LOADS; ++j) {
+    const int r = (wid * B_LOADS + j) * 8 + (lane >> 3);
+    const int c = (lane & 7) ^ swz_key(r);
+    o.b[j] = (uint32_t)r * (uint32_t)it.K + (uint32_t)c * 16u;
+  }
+  const int r = wid * 64 + lane;
+  o.scale_row = r < it.live ? r : it.live - 1;
+  return o;
+}
+
+// Issue the direct-to-LDS loads of K step kb into `stage`.  A wave skips the
+// activation loads whose 8 rows are all alignment padding (rows past the
+// live rows inside a loaded 8-row block reload the last live row); the number
+// of loads a wave issues per stage is the same for every stage of an item
+// (stage_loads), which is what its vmcnt waits count on.
+__device__ __forceinline__ void issue_stage(const Item& it, const LoadOffsets& o, uint8_t* stage,
+                                            int kb, int wid) {
 #ifdef PROBE_NO_LOADS
   return;
 #endif
+  const uint8_t* abase = it.a + kb * BK;
+  const uint8_t* bbase = it.b + kb * BK;
 #pragma unroll
   for (int j = 0; j < A_LOADS; ++j) {
     const int base = (wid * A_LOADS + j) * 8;  // 8 rows per wave instruction
-    const int r = base + (lane >> 3);
-    const int c = (lane & 7) ^ (r & 7);
-    const int rr = r < it.live ? r : it.live - 1;
-    dma16(it.a + (int64_t)rr * it.K + kb * BK + c * 16, lds_addr(stage + base * 128));
+    if (base >= it.live) break;                // only padding rows: not loaded
+    dma16(abase, o.a[j], lds_addr(stage + base * 128));
   }
 #pragma unroll
   for (int j = 0; j < B_LOADS; ++j) {
     const int base = (wid * B_LOADS + j) * 8;
-    const int r = base + (lane >> 3);
-    const int c = (lane & 7) ^ (r & 7);
-    dma16(it.b + (int64_t)r * it.K + kb * BK + c * 16, lds_addr(stage + A_BYTES + base * 128));
+    dma16(bbase, o.b[j], lds_addr(stage + A_BYTES + base * 128));
   }
   // Scales: the aligned dword holding each element (UE8M0 bytes are picked
   // out of it when used).  Waves 0-3: one activation row each lane; waves
   // 4-7: a copy of the weight block scale.
   if (wid < 4) {
-    const int r = wid * 64 + lane;
-    const int rr = r < it.live ? r : it.live - 1;
-    const int64_t off = (it.as0 + (int64_t)rr * it.KB + kb) * it.sbytes;
-    dma4(it.as + (off & ~(int64_t)3), lds_addr(stage + A_BYTES + B_BYTES + wid * 256));
+    const int64_t off = (it.as0 + (int64_t)o.scale_row * it.KB + kb) * it.sbytes;
+    dma4(it.as, (uint32_t)(off & ~(int64_t)3), lds_addr(stage + A_BYTES + B_BYTES + wid * 256));
   } else {
-    const int64_t boff = (it.bs0 + kb) * it.sbytes;
-    dma4(it.bs + (boff & ~(int64_t)3),
-         lds_addr(stage + A_BYTES + B_BYTES + SA_BYTES + (wid - 4) * 256));
+    const int64_t boff = ((it.bs0 + kb) * it.sbytes) & ~(int64_t)3;
+    dma4(it.bs + boff, 0u, lds_addr(stage + A_BYTES + B_BYTES + SA_BYTES + (wid - 4) * 256));
   }
 }
 
-__device__ __forceinline__ v8i frag(const uint8_t* tile, int r, int fk) {
+// Per-lane LDS byte offsets (within a stage) of the two 16-byte halves of
+// this lane's A and B fragments for row/column tile 0; tile i adds i * 2048.
+struct FragOffsets {
+  int a_lo, a_hi, b_lo, b_hi, s_row;
+};
+
+__device__ __forceinline__ FragOffsets frag_offsets(int lane, int wm, int wn) {
+  const int frow = lane & 15, fk = (lane >> 4) * 2;
+  FragOffsets f;
+  const int ra = wm * WTM + frow, rb = wn * WTN + frow;
+  f.a_lo = swz(ra, fk);
+  f.a_hi = swz(ra, fk + 1);
+  f.b_lo = A_BYTES + swz(rb, fk);
+  f.b_hi = A_BYTES + swz(rb, fk + 1);
+  f.s_row = wm * WTM + (lane >> 4) * 4;  // first output row of this lane
+  return f;
+}
+
+__device__ __forceinline__ v8i frag2(const uint8_t* stage, int lo_off, int hi_off) {
   typedef unsigned int u4 __attribute__((ext_vector_type(4)));
-  const u4 lo = *reinterpret_cast<const u4*>(tile + swz(r, fk));
-  const u4 hi = *reinterpret_cast<const u4*>(tile + swz(r, fk + 1));
+  const u4 lo = *reinterpret_cast<const u4*>(stage + lo_off);
+  const u4 hi = *reinterpret_cast<const u4*>(stage + hi_off);
   return v8i{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3], (int)hi[0], (int)hi[1], (int)hi[2],
              (int)hi[3]};
 }
@@ -156,28 +225,27 @@ __device__ __forceinline__ v4f mfma_plain(const v8i& a, const v8i& b) {
                                                           127, 0, 127);
 }
 
-template <bool kUe8m0>
+// NFM: how many of the wave's four 16-row tiles hold live rows.
+template <bool kUe8m0, int NFM>
 __device__ __forceinline__ void compute_stage(const uint8_t* stage, v4f (&acc)[FM][FN],
-                                              const Item& it, int kb, int lane, int wm,
-                                              int wn) {
+                                              const Item& it, const FragOffsets& fo, int kb,
+                                              int lane, int nfm_rt) {
 #ifdef PROBE_NO_COMPUTE
   return;
 #endif
-  const uint8_t* sa = stage;
-  const uint8_t* sb = stage + A_BYTES;
   const uint32_t* ssa = reinterpret_cast<const uint32_t*>(stage + A_BYTES + B_BYTES);
   const uint32_t* ssb = reinterpret_cast<const uint32_t*>(stage + A_BYTES + B_BYTES + SA_BYTES);
-  const int frow = lane & 15, fk = (lane >> 4) * 2;
-  const int r0 = wm * WTM;
   v8i bf[FN];
 #pragma unroll
-  for (int j = 0; j < FN; ++j) bf[j] = frag(sb, wn * WTN + j * 16 + frow, fk);
+  for (int j = 0; j < FN; ++j) bf[j] = frag2(stage + j * 2048, fo.b_lo, fo.b_hi);
   if constexpr (kUe8m0) {
     const int sbyte = (int)((ssb[0] >> (8 * (int)((it.bs0 + kb) & 3))) & 0xffu);
+    const int arow = fo.s_row - (lane >> 4) * 4 + (lane & 15);  // this lane's A row
 #pragma unroll
     for (int i = 0; i < FM; ++i) {
-      const int r = r0 + i * 16 + frow;
-      const v8i af = frag(sa, r, fk);
+      if (i >= nfm_rt) break;  // uniform per wave
+      const int r = arow + i * 16;
+      const v8i af = frag2(stage + i * 2048, fo.a_lo, fo.a_hi);
       const int apos = (int)((it.as0 + (int64_t)r * it.KB + kb) & 3);
       const int abyte = (int)((ssa[r] >> (8 * apos)) & 0xffu);
 #pragma unroll
@@ -191,27 +259,43 @@ __device__ __forceinline__ void compute_stage(const uint8_t* stage, v4f (&acc)[F
     // while the VALU scales and accumulates.
     const float sbv = __uint_as_float(ssb[0]);
     v4f p[2][FN];
-    {
-      const v8i af = frag(sa, r0 + frow, fk);
+    if constexpr (NFM > 0) {
+      const v8i af = frag2(stage, fo.a_lo, fo.a_hi);
 #pragma unroll
       for (int j = 0; j < FN; ++j) p[0][j] = mfma_plain(af, bf[j]);
     }
 #pragma unroll
-    for (int i = 0; i < FM; ++i) {
-      if (i + 1 < FM) {
-        const v8i af = frag(sa, r0 + (i + 1) * 16 + frow, fk);
+    for (int i = 0; i < NFM; ++i) {
+      if (i + 1 < NFM) {
+        const v8i af = frag2(stage + (i + 1) * 2048, fo.a_lo, fo.a_hi);
 #pragma unroll
         for (int j = 0; j < FN; ++j) p[(i + 1) & 1][j] = mfma_plain(af, bf[j]);
       }
       float sc[4];
 #pragma unroll
-      for (int q = 0; q < 4; ++q)
-        sc[q] = __uint_as_float(ssa[r0 + i * 16 + (lane >> 4) * 4 + q]) * sbv;
+      for (int q = 0; q < 4; ++q) sc[q] = __uint_as_float(ssa[fo.s_row + i * 16 + q]) * sbv;
 #pragma unroll
       for (int j = 0; j < FN; ++j)
 #pragma unroll
         for (int q = 0; q < 4; ++q) acc[i][j][q] += p[i & 1][j][q] * sc[q];
     }
+  }
+}
+
+// The K loop of one item: wait for stage kb (this wave's loads; the barrier
+// makes every wave's visible and retires the stage read one step ago), refill
+// that older stage with step kb+2, compute on stage kb.
+template <bool kUe8m0, int NFM>
+__device__ __forceinline__ void kloop(uint8_t* lds, v4f (&acc)[FM][FN], const Item& it,
+                                      const LoadOffsets& lo_, const FragOffsets& fo, int lane,
+                                      int wid, int nfm, int stage_loads) {
+  for (int kb = 0; kb < it.KB; ++kb) {
+    if (kb + 1 < it.KB) wait_vmcnt_rt(stage_loads);
+    else wait_vmcnt<0>();
+    barrier();
+    if (kb + 2 < it.KB) issue_stage(it, lo_, lds + ((kb + 2) % kStages) * STAGE, kb + 2, wid);
+    if (NFM > 0 || (kUe8m0 && nfm > 0))
+      compute_stage<kUe8m0, NFM>(lds + (kb % kStages) * STAGE, acc, it, fo, kb, lane, nfm);
   }
 }
 
@@ -225,6 +309,7 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(
   __shared__ int gp[MOE_MAX_EXPERTS + 1];  // prefix of row groups per expert
   const int t = threadIdx.x, lane = t & 63, wid = t >> 6;
   const int wm = wid / WAVES_N, wn = wid % WAVES_N;
+  const FragOffsets fo = frag_offsets(lane, wm, wn);
   const int64_t nrows = min((int64_t)status[0], capacity);
   const int sbytes = kUe8m0 ? 1 : 4;
   const int KB = K / BK, NT = N / BN;
@@ -276,7 +361,10 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(
     it.bs = w_scale;
     it.as0 = m0 * KB;
     it.bs0 = ((int64_t)e * NT + nt) * KB;
-    const bool active = wm * WTM < it.live;  // this wave's rows hold slots
+    // Live 16-row MFMA tiles of this wave, and the loads it issues per stage.
+    const int nfm = (int)max(0, min(FM, (it.live - wm * WTM + 15) / 16));
+    const int na = (int)max(0, min(A_LOADS, (it.live - wid * A_LOADS * 8 + 7) / 8));
+    const int stage_loads = na + B_LOADS + 1;
 
     v4f acc[FM][FN];
 #pragma unroll
@@ -284,16 +372,20 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(
 #pragma unroll
       for (int j = 0; j < FN; ++j) acc[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
 
+    const LoadOffsets lo_ = load_offsets(it, lane, wid);
     wait_vmcnt<0>();  // nothing older (previous item's stores) left in flight
-    issue_stage(it, lds, 0, lane, wid);
-    if (KB > 1) issue_stage(it, lds + STAGE, 1, lane, wid);
-    for (int kb = 0; kb < KB; ++kb) {
-      if (kb + 1 < KB) wait_vmcnt<LOADS_PER_STAGE>();
-      else wait_vmcnt<0>();
-      barrier();  // stage kb landed for every wave; stage kb-1 fully consumed
-      if (kb + 2 < KB) issue_stage(it, lds + ((kb + 2) % kStages) * STAGE, kb + 2, lane, wid);
-      if (active)
-        compute_stage<kUe8m0>(lds + (kb % kStages) * STAGE, acc, it, kb, lane, wm, wn);
+    issue_stage(it, lo_, lds, 0, wid);
+    if (KB > 1) issue_stage(it, lo_, lds + STAGE, 1, wid);
+    if constexpr (kUe8m0) {
+      kloop<true, FM>(lds, acc, it, lo_, fo, lane, wid, nfm, stage_loads);
+    } else {
+      switch (nfm) {  // uniform per wave; one K loop per live-tile count
+        case 4: kloop<false, 4>(lds, acc, it, lo_, fo, lane, wid, 4, stage_loads); break;
+        case 3: kloop<false, 3>(lds, acc, it, lo_, fo, lane, wid, 3, stage_loads); break;
+        case 2: kloop<false, 2>(lds, acc, it, lo_, fo, lane, wid, 2, stage_loads); break;
+        case 1: kloop<false, 1>(lds, acc, it, lo_, fo, lane, wid, 1, stage_loads); break;
+        default: kloop<false, 0>(lds, acc, it, lo_, fo, lane, wid, 0, stage_loads); break;
+      }
     }
     barrier();  // every wave is done reading the stages
 

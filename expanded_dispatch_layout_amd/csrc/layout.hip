@@ -9,30 +9,32 @@
 // real/padding boundary, zeroed alignment gaps).
 //
 // Three kernels on one stream:
-//  1. count   one thread per row; per-32-row-group expert counts (LDS
-//             atomics, order-free) -> workspace.
-//  2. scan    one workgroup: per-expert exclusive scan over the groups
-//             (one wave per expert column), then the expert starts as the
-//             exclusive scan of the aligned counts (start[e] is the sum of
-//             align(count) over e' < e, because every start is aligned),
-//             psum, total and flags.
-//  3. scatter one workgroup per 32-row group.  Wave 0 ranks the group's
-//             slots in ascending (row, k) order per expert (wave min over
-//             the experts present, then a lane prefix sum of per-row
-//             counts), giving src2dst; then all four waves copy each source
-//             row once to every destination with 16-byte loads/stores.
-//             The same grid zero-fills the alignment pad rows and writes the
-//             row labels (grid-stride), so no extra pass is needed.
+//  1. count   one thread per received row; order-free per-expert counts of
+//             every 16-row group (LDS atomics) -> workspace.
+//  2. scan    one workgroup: per-expert exclusive scan over the groups (one
+//             wave per expert column), then the expert starts as the
+//             exclusive scan of the aligned counts (every start is aligned,
+//             so start[e] = sum of align(count) over e' < e), psum, total,
+//             flags.
+//  3. scatter one wave per received row.  The stable rank of slot (r, k)
+//             among its expert's slots is the group's offset plus the number
+//             of that expert's slots in the earlier rows of the group plus
+//             those at k' < k in row r: two ballots over the group's ids.
+//             Destination = start[e] + rank; the row (16-byte chunks) and its
+//             scales are read once and written to each destination.  The
+//             same grid zero-fills the alignment pad rows and writes the row
+//             labels (grid-stride), so no extra pass is needed.
 #include "common.hpp"
 
 namespace moe {
 namespace {
 
-constexpr int kGroupRows = 32;     // rows ranked together (one wave)
-constexpr int kCountThreads = 256; // rows per count workgroup
-constexpr int kGroupsPerCount = kCountThreads / kGroupRows;
+constexpr int kGroupRows = 16;     // rows per counted group
+constexpr int kCountThreads = 256; // one row per thread: 16 groups per workgroup
+constexpr int kGroupsPerBlock = kCountThreads / kGroupRows;
 constexpr int kScanThreads = 1024;
 constexpr int kScatterThreads = 256;
+constexpr int kRowsPerScatterBlock = kScatterThreads / 64;
 
 struct Workspace {
   int32_t* grp;       // [ngroups][E]: counts, then exclusive offsets
@@ -71,32 +73,31 @@ __global__ __launch_bounds__(kCountThreads) void expand_count_kernel(
     const int32_t* __restrict__ ids, const int32_t* __restrict__ psum_rank, int nsrc,
     int64_t rows, int topk, int E, int64_t ngroups, int32_t* __restrict__ grp,
     int32_t* __restrict__ grp_flag) {
-  extern __shared__ int32_t lds_cnt[];  // [kGroupsPerCount][E] then flags
-  int32_t* lflag = lds_cnt + kGroupsPerCount * E;
+  extern __shared__ int32_t cnt[];  // [kGroupsPerBlock][E], then flags
+  int32_t* lflag = cnt + kGroupsPerBlock * E;
   const int t = threadIdx.x;
-  for (int i = t; i < kGroupsPerCount * E; i += kCountThreads) lds_cnt[i] = 0;
-  if (t < kGroupsPerCount) lflag[t] = 0;
+  for (int i = t; i < kGroupsPerBlock * E; i += kCountThreads) cnt[i] = 0;
+  if (t < kGroupsPerBlock) lflag[t] = 0;
   __syncthreads();
   const int64_t nv = valid_rows(psum_rank, nsrc, rows);
   const int64_t r = (int64_t)blockIdx.x * kCountThreads + t;
   const int g = t / kGroupRows;
   if (r < nv) {
     int bad = 0;
-    const int32_t* row = ids + r * topk;
     for (int k = 0; k < topk; ++k) {
-      int e = row[k];
+      const int e = ids[r * topk + k];
       if (e >= E) bad = 1;
-      else if (e >= 0) atomicAdd(&lds_cnt[g * E + e], 1);
+      else if (e >= 0) atomicAdd(&cnt[g * E + e], 1);
     }
     if (bad) atomicOr(&lflag[g], MOE_FLAG_EXPERT_ID_RANGE);
   }
   __syncthreads();
-  const int64_t g0 = (int64_t)blockIdx.x * kGroupsPerCount;
-  for (int i = t; i < kGroupsPerCount * E; i += kCountThreads) {
-    int64_t gg = g0 + i / E;
-    if (gg < ngroups) grp[gg * E + (i % E)] = lds_cnt[i];
+  const int64_t g0 = (int64_t)blockIdx.x * kGroupsPerBlock;
+  for (int i = t; i < kGroupsPerBlock * E; i += kCountThreads) {
+    const int64_t gg = g0 + i / E;
+    if (gg < ngroups) grp[gg * E + i % E] = cnt[i];
   }
-  if (t < kGroupsPerCount && g0 + t < ngroups) grp_flag[g0 + t] = lflag[t];
+  if (t < kGroupsPerBlock && g0 + t < ngroups) grp_flag[g0 + t] = lflag[t];
 }
 
 // Exclusive scan over the whole 1024-thread workgroup; returns the exclusive
@@ -183,118 +184,93 @@ __global__ __launch_bounds__(kScatterThreads) void expand_scatter_kernel(
     const int32_t* __restrict__ status, uint8_t* __restrict__ ex, uint8_t* __restrict__ ex_scale,
     int32_t* __restrict__ m_indices, int32_t* __restrict__ src2dst, float* __restrict__ row_weight) {
   extern __shared__ int32_t lds[];
-  int32_t* l_starts = lds;                       // [E]
-  int32_t* l_padbase = l_starts + E;             // [E + 1]
-  int32_t* l_ids = l_padbase + E + 1;            // [kGroupRows][topk]
-  int32_t* l_dst = l_ids + kGroupRows * topk;    // [kGroupRows][topk]
-  int32_t* l_live = l_dst + kGroupRows * topk;   // [kGroupRows]
+  int32_t* l_starts = lds;            // [E]
+  int32_t* l_padbase = l_starts + E;  // [E + 1]
   const int t = threadIdx.x, lane = t & 63, wid = t >> 6;
-  const int64_t g = blockIdx.x;
+  for (int i = t; i < E; i += kScatterThreads) l_starts[i] = starts_g[i];
+  for (int i = t; i <= E; i += kScatterThreads) l_padbase[i] = padbase_g[i];
+  __syncthreads();
   const int64_t nv = valid_rows(psum_rank, nsrc, rows);
   const int total = status[0];
   const int64_t nrows_ex = min((int64_t)total, capacity);
+  const int nsc = hidden / kGroup;
+  const int nch = hidden / 16;
+  const int64_t gwaves = (int64_t)gridDim.x * (kScatterThreads / 64);
+  const int64_t wave0 = (int64_t)blockIdx.x * (kScatterThreads / 64) + wid;
 
-  for (int i = t; i < E; i += kScatterThreads) l_starts[i] = starts_g[i];
-  for (int i = t; i <= E; i += kScatterThreads) l_padbase[i] = padbase_g[i];
-  const int64_t r0 = g * kGroupRows;
-  if (g < num_groups(rows)) {
-    for (int i = t; i < kGroupRows * topk; i += kScatterThreads) {
-      int64_t r = r0 + i / topk;
-      l_ids[i] = (r < nv) ? ids[r0 * topk + i] : -1;
-      l_dst[i] = -1;
+  // ---- one wave per received row ----
+  for (int64_t r = wave0; r < rows; r += gwaves) {
+    const int64_t g = r / kGroupRows;
+    const int64_t g_first = g * kGroupRows;
+    // Ids of the earlier rows of this group (up to 15 * topk <= 480 values,
+    // eight per lane), and of this row (lane k < topk holds slot k).
+    const int nprev = (int)(r - g_first) * topk;
+    int prev[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int idx = i * 64 + lane;
+      prev[i] = (idx < nprev && g_first + idx / topk < nv) ? ids[g_first * topk + idx] : -1;
     }
-  }
-  __syncthreads();
-
-  if (g < num_groups(rows)) {
-    // ---- rank (wave 0): stable order (row, k) within each expert ----
-    if (wid == 0) {
-      const bool valid = lane < kGroupRows && r0 + lane < nv;
-      const int32_t* my = l_ids + (lane < kGroupRows ? lane : 0) * topk;
-      int32_t* myd = l_dst + (lane < kGroupRows ? lane : 0) * topk;
-      int last = -1, nlive = 0;
-      for (;;) {
-        int mine = 0x7fffffff;
-        if (valid)
-          for (int k = 0; k < topk; ++k) {
-            int e = my[k];
-            if (e > last && e < E && e < mine) mine = e;
-          }
-        const int emin = wave_min_i(mine);
-        if (emin == 0x7fffffff) break;
-        int c = 0;
-        if (valid)
-          for (int k = 0; k < topk; ++k) c += (my[k] == emin);
-        const int pre = wave_incl_scan_i(c) - c;
-        const int base = l_starts[emin] + grp_off[g * E + emin];
-        if (c) {
-          int j = 0;
-          for (int k = 0; k < topk; ++k) {
-            if (my[k] == emin) {
-              int64_t d = (int64_t)base + pre + j++;
-              if (d < capacity) {
-                myd[k] = (int)d;
-                ++nlive;
-                if (row_weight) row_weight[d] = topk_w[(r0 + lane) * topk + k];
-              }
-            }
-          }
-        }
-        last = emin;
+    const int myid = (lane < topk && r < nv) ? ids[r * topk + lane] : -1;
+    int d = -1;
+    const uint64_t live = __ballot(myid >= 0 && myid < E);
+    for (uint64_t mm = live; mm; mm &= mm - 1) {
+      const int k = __builtin_ctzll(mm);
+      const int e = __shfl(myid, k, 64);
+      int rank = __popcll(__ballot(myid == e) & ((1ull << k) - 1ull));  // k' < k
+#pragma unroll
+      for (int i = 0; i < 8; ++i) rank += __popcll(__ballot(prev[i] == e));
+      const int64_t dd = (int64_t)l_starts[e] + grp_off[g * E + e] + rank;
+      if (lane == k && dd < capacity) {
+        d = (int)dd;
+        if (row_weight) row_weight[d] = topk_w[r * topk + k];
       }
-      if (lane < kGroupRows) l_live[lane] = nlive;
     }
-    __syncthreads();
-    // src2dst for every row of the group (rows >= R_v get -1 everywhere)
-    for (int i = t; i < kGroupRows * topk; i += kScatterThreads) {
-      int64_t r = r0 + i / topk;
-      if (r < rows) src2dst[r0 * topk + i] = l_dst[i];
-    }
-    // ---- copy: one wave per source row, 16-byte chunks, read once ----
-    const int nch = hidden / 16;
-    for (int i = wid; i < kGroupRows; i += kScatterThreads / 64) {
-      if (l_live[i] == 0) continue;
-      const int64_t r = r0 + i;
-      const u32x4* src = reinterpret_cast<const u32x4*>(x + r * x_stride);
-      const int32_t* dl = l_dst + i * topk;
-      for (int c0 = 0; c0 < nch; c0 += 64 * 4) {
-        u32x4 v[4];
+    if (lane < topk) src2dst[r * topk + lane] = d;
+    uint64_t mask = __ballot(d >= 0);
+    if (mask == 0) continue;
+    const u32x4* src = reinterpret_cast<const u32x4*>(x + r * x_stride);
+    for (int c0 = 0; c0 < nch; c0 += 64 * 8) {
+      u32x4 v[8];
 #pragma unroll
-        for (int u = 0; u < 4; ++u) {
-          int c = c0 + u * 64 + lane;
-          if (c < nch) v[u] = src[c];
-        }
-        for (int k = 0; k < topk; ++k) {
-          const int d = dl[k];
-          if (d < 0) continue;
-          u32x4* dst = reinterpret_cast<u32x4*>(ex + (int64_t)d * hidden);
+      for (int u = 0; u < 8; ++u) {
+        const int c = c0 + u * 64 + lane;
+        if (c < nch) v[u] = src[c];
+      }
+      for (uint64_t mm = mask; mm; mm &= mm - 1) {
+        const int k = __builtin_ctzll(mm);
+        const int dk = __shfl(d, k, 64);
+        u32x4* dst = reinterpret_cast<u32x4*>(ex + (int64_t)dk * hidden);
 #pragma unroll
-          for (int u = 0; u < 4; ++u) {
-            int c = c0 + u * 64 + lane;
-            if (c < nch) dst[c] = v[u];
-          }
+        for (int u = 0; u < 8; ++u) {
+          const int c = c0 + u * 64 + lane;
+          if (c < nch) dst[c] = v[u];
         }
       }
-      const int nsc = hidden / kGroup;
-      for (int c = lane; c < nsc; c += 64) {
-        if (scale_bytes == 4) {
-          const float s = reinterpret_cast<const float*>(x_scale + r * x_scale_stride_bytes)[c];
-          for (int k = 0; k < topk; ++k) {
-            const int d = dl[k];
-            if (d >= 0) reinterpret_cast<float*>(ex_scale + (int64_t)d * nsc * 4)[c] = s;
-          }
-        } else {
-          const uint8_t s = (x_scale + r * x_scale_stride_bytes)[c];
-          for (int k = 0; k < topk; ++k) {
-            const int d = dl[k];
-            if (d >= 0) (ex_scale + (int64_t)d * nsc)[c] = s;
-          }
+    }
+    // Scales: the shuffles run with every lane active (a lane-divergent
+    // shuffle could read an inactive lane), the stores only where c < nsc.
+    for (int c0 = 0; c0 < nsc; c0 += 64) {
+      const int c = c0 + lane;
+      float sf = 0.f;
+      uint8_t sb = 0;
+      if (c < nsc) {
+        if (scale_bytes == 4)
+          sf = reinterpret_cast<const float*>(x_scale + r * x_scale_stride_bytes)[c];
+        else
+          sb = (x_scale + r * x_scale_stride_bytes)[c];
+      }
+      for (uint64_t mm = mask; mm; mm &= mm - 1) {
+        const int dk = __shfl(d, __builtin_ctzll(mm), 64);
+        if (c < nsc) {
+          if (scale_bytes == 4) reinterpret_cast<float*>(ex_scale + (int64_t)dk * nsc * 4)[c] = sf;
+          else (ex_scale + (int64_t)dk * nsc)[c] = sb;
         }
       }
     }
   }
 
-  // ---- grid-stride: alignment pad rows and row labels ----
+  // ---- grid-stride: row labels and alignment pad rows ----
   const int64_t gthreads = (int64_t)gridDim.x * kScatterThreads;
   const int64_t gtid = (int64_t)blockIdx.x * kScatterThreads + t;
   for (int64_t i = gtid; i < capacity; i += gthreads) {
@@ -303,15 +279,13 @@ __global__ __launch_bounds__(kScatterThreads) void expand_scatter_kernel(
     m_indices[i] = lab;
   }
   const int npad = l_padbase[E];
-  const int64_t gwaves = (int64_t)gridDim.x * (kScatterThreads / 64);
-  const int nsc = hidden / kGroup;
-  for (int64_t p = (int64_t)blockIdx.x * (kScatterThreads / 64) + wid; p < npad; p += gwaves) {
+  for (int64_t p = wave0; p < npad; p += gwaves) {
     const int e = last_le(l_padbase, E, (int)p);
     const int64_t row = (int64_t)psum_g[e] + (p - l_padbase[e]);
     if (row >= capacity) continue;
     u32x4* dst = reinterpret_cast<u32x4*>(ex + row * hidden);
     const u32x4 z = {0u, 0u, 0u, 0u};
-    for (int c = lane; c < hidden / 16; c += 64) dst[c] = z;
+    for (int c = lane; c < nch; c += 64) dst[c] = z;
     for (int c = lane; c < nsc * scale_bytes; c += 64) ex_scale[row * nsc * scale_bytes + c] = 0;
     if (lane == 0 && row_weight) row_weight[row] = 0.f;
   }
@@ -363,7 +337,7 @@ extern "C" moe_status moe_expand_layout(
 
   if (ng > 0) {
     const int64_t nblk = (rows + kCountThreads - 1) / kCountThreads;
-    size_t lds = size_t(kGroupsPerCount) * E * 4 + kGroupsPerCount * 4;
+    const size_t lds = size_t(kGroupsPerBlock) * (E + 1) * 4;
     hipLaunchKernelGGL(expand_count_kernel, dim3((unsigned)nblk), dim3(kCountThreads), lds, s,
                        topk_ids, psum_recv_per_rank, num_src_ranks, rows, topk, E, ng, w.grp,
                        w.grp_flag);
@@ -373,12 +347,12 @@ extern "C" moe_status moe_expand_layout(
                      E, align, capacity, w.starts, w.padbase, psum, status);
   if (hipGetLastError() != hipSuccess) return MOE_ERR_LAUNCH;
 
-  // Enough workgroups to cover the row groups, and at least a few hundred so
-  // the label fill and pad zeroing spread over the chip.
-  int64_t grid = ng;
-  const int64_t min_grid = 512;
-  if (grid < min_grid) grid = min_grid;
-  size_t lds = size_t(E) * 4 + size_t(E + 1) * 4 + size_t(kGroupRows) * topk * 8 + kGroupRows * 4;
+  // One wave per received row, and enough workgroups that the label fill and
+  // the pad zeroing spread over the chip.
+  int64_t grid = (rows + kRowsPerScatterBlock - 1) / kRowsPerScatterBlock;
+  if (grid < 1024) grid = 1024;
+  if (grid > 16384) grid = 16384;
+  const size_t lds = size_t(E) * 4 + size_t(E + 1) * 4;
   hipLaunchKernelGGL(expand_scatter_kernel, dim3((unsigned)grid), dim3(kScatterThreads), lds, s,
                      (const uint8_t*)x, x_stride, (const uint8_t*)x_scale,
                      x_scale_stride * scale_bytes, scale_bytes, topk_ids, topk_weights,

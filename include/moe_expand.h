@@ -225,7 +225,8 @@ moe_status moe_act_quant(
  *   c_k * float(expert_out[src2dst[r,k]]) ), c_k = topk_weights[r,k] or 1,
  * each product and sum rounded to fp32 in that order.  Valid rows with no
  * live slot become 0.  Rows >= R_v are not written.
- * Sizes: hidden % 128 == 0; buffers 16-byte aligned.
+ * Sizes: hidden % 128 == 0 and hidden <= 8192 (else MOE_ERR_UNSUPPORTED);
+ * buffers 16-byte aligned.
  */
 moe_status moe_gather(
     const void* expert_out, const int32_t* src2dst, const float* topk_weights,
