@@ -12,8 +12,8 @@ generator on the GPU and quantised to fp8 with 1x128 / 128x128 scales by
 plain torch ops: input preparation, not part of the timed path).
 
 Prints one JSON line.  Extra keys: per-stage microseconds, the roofline of
-the dominant kernel (gate_up GEMM) and the CPU oracle's throughput on the
-host's cores.
+the dominant kernel (the grouped fp8 GEMM, both of its launches) and the CPU
+oracle's throughput on the host's cores.
 """
 
 import argparse
@@ -38,6 +38,10 @@ def parse():
     p.add_argument("--workload", default="dsv3")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-runs", type=int, default=3)
+    p.add_argument("--pmc-target", choices=["gemm", "copy"], default=None,
+                   help="profiling mode: run only this kernel a few times (for rocprofv3 "
+                        "--pmc); 'copy' is a plain 256 MiB device copy used to calibrate "
+                        "the byte counters")
     return p.parse_args()
 
 
@@ -110,6 +114,36 @@ def make_inputs(wl, device):
                 w2=w2q, w2_scale=w2s, num_valid=nv, data=d)
 
 
+def measured_traffic(workload):
+    """Measured HBM bytes per launch of the grouped GEMM kernel (mean over its
+    gate_up and down launches) from the committed PMC summary
+    profiles/grouped_gemm_<workload>_pmc.txt, or None when there is none or
+    the kernel source has changed since the counters were taken."""
+    import hashlib
+    path = os.path.join(ROOT, "profiles", f"grouped_gemm_{workload}_pmc.txt")
+    src = os.path.join(ROOT, "expanded_dispatch_layout_amd", "csrc", "gemm.hip")
+    if not os.path.exists(path):
+        return None
+    rec = {}
+    for line in open(path):
+        if ":" in line and not line.startswith(" "):
+            k, v = line.split(":", 1)
+            rec[k.strip()] = v.strip()
+    sha = hashlib.sha256(open(src, "rb").read()).hexdigest()[:16]
+    if rec.get("gemm_source_sha256_16") != sha or "traffic_bytes_per_launch" not in rec:
+        return None
+    return int(rec["traffic_bytes_per_launch"])
+
+
+def gemm_cost(rows, n, k, nonempty, sbytes):
+    """Algorithmic HBM bytes and useful flops of one grouped GEMM launch: each
+    non-empty expert's weights and block scales once, the live rows' fp8
+    activations and scales once, their bf16 outputs once."""
+    weights = nonempty * (n * k + (n // 128) * (k // 128) * sbytes)
+    acts = rows * (k + (k // 128) * sbytes)
+    return weights + acts + rows * n * 2, 2.0 * rows * n * k
+
+
 def cpu_baseline(inp, wl, runs):
     """The oracle as it stands, on this host's cores, over the same inputs."""
     import numpy as np
@@ -151,6 +185,15 @@ def main():
 
     wl = W.workload(args.workload)
     dev = "cuda"
+    if args.pmc_target == "copy":
+        src = torch.empty(256 << 20, dtype=torch.uint8, device=dev).fill_(1)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"pmc_target": "copy", "bytes_read": src.numel(),
+                          "bytes_written": dst.numel()}))
+        return
     inp = make_inputs(wl, dev)
     mod = M.ExpandedMoE(wl.rows, wl.topk, inp["w13"], inp["w13_scale"], inp["w2"],
                         inp["w2_scale"], wl.align, wl.fmt, device=dev)
@@ -172,14 +215,23 @@ def main():
         else:
             mod.gather(inp["w"], inp["prank"], out)
 
+    if args.pmc_target == "gemm":     # layout once, then 3 x (gate_up, act, down)
+        stage(0)
+        for _ in range(3):
+            for i in (1, 2, 3):
+                stage(i)
+        torch.cuda.synchronize()
+        print(json.dumps({"pmc_target": "gemm", "status": mod.status.cpu().tolist()}))
+        return
+
     for _ in range(args.warmup):
         for i in range(5):
             stage(i)
     torch.cuda.synchronize()
 
-    # Timed region: K whole steps; events only around the dominant kernel.
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-          for _ in range(args.steps)]
+    # Timed region: K whole steps; events around the dominant kernel's two
+    # launches (gate_up, down), recorded on the stream the kernels run on.
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
     t_start = torch.cuda.Event(enable_timing=True)
     t_end = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
@@ -190,13 +242,16 @@ def main():
         stage(1)
         ev[s][1].record()
         stage(2)
+        ev[s][2].record()
         stage(3)
+        ev[s][3].record()
         stage(4)
     t_end.record()
     torch.cuda.synchronize()
     total_ms = t_start.elapsed_time(t_end)
     ms_step = total_ms / args.steps
-    gemm1_us = float(np.mean([a.elapsed_time(b) for a, b in ev])) * 1e3
+    gemm1_us = float(np.mean([e[0].elapsed_time(e[1]) for e in ev])) * 1e3
+    gemm2_us = float(np.mean([e[2].elapsed_time(e[3]) for e in ev])) * 1e3
 
     # Per-stage breakdown (after the timed region; events between stages).
     sev = [[torch.cuda.Event(enable_timing=True) for _ in range(6)] for _ in range(10)]
@@ -218,24 +273,26 @@ def main():
     nonempty = int((counts > 0).sum())
     H, I = wl.hidden, wl.inter
     sb = 4 if wl.fmt == "f32" else 1
-    g1_bytes = (nonempty * (2 * I * H + (2 * I // 128) * (H // 128) * sb)
-                + m_used * (H + H // 128 * sb) + m_used * 2 * I * 2)
-    g1_flops = 2.0 * A * 2 * I * H
-    t = gemm1_us * 1e-6
-    hbm_time = g1_bytes / (HBM_PEAK_GBS * 1e9)
-    mfma_time = g1_flops / (FP8_PEAK_TFLOPS * 1e12)
-    if hbm_time >= mfma_time:
-        roof = {"bound": "hbm", "achieved": g1_bytes / t / 1e9, "peak": HBM_PEAK_GBS,
+    # Dominant kernel: the grouped GEMM, averaged over its two launches per
+    # step (gate_up [A, 2I] x K=H, then down [A, H] x K=I; A = live rows).
+    g1_bytes, g1_flops = gemm_cost(A, 2 * I, H, nonempty, sb)
+    g2_bytes, g2_flops = gemm_cost(A, H, I, nonempty, sb)
+    t = (gemm1_us + gemm2_us) * 1e-6
+    byts, flops = g1_bytes + g2_bytes, g1_flops + g2_flops
+    if byts / (HBM_PEAK_GBS * 1e9) >= flops / (FP8_PEAK_TFLOPS * 1e12):
+        roof = {"bound": "hbm", "achieved": byts / t / 1e9, "peak": HBM_PEAK_GBS,
                 "unit": "GB/s"}
     else:
-        roof = {"bound": "mfma", "achieved": g1_flops / t / 1e12, "peak": FP8_PEAK_TFLOPS,
+        roof = {"bound": "mfma", "achieved": flops / t / 1e12, "peak": FP8_PEAK_TFLOPS,
                 "unit": "TFLOP/s"}
     roof["frac"] = roof["achieved"] / roof["peak"]
-    roof["traffic"] = None
-    roof["kernel"] = "grouped_gemm_kernel (gate_up)"
-    roof["kernel_us"] = gemm1_us
-    roof["algorithmic_bytes"] = int(g1_bytes)
-    roof["useful_flops"] = g1_flops
+    roof["traffic"] = measured_traffic(wl.name)
+    roof["kernel"] = (f"grouped_gemm_kernel<{str(wl.fmt == 'ue8m0').lower()}> "
+                      "(mean over its gate_up and down launches)")
+    roof["launch_us"] = {"gate_up": gemm1_us, "down": gemm2_us, "mean": (gemm1_us + gemm2_us) / 2}
+    roof["algorithmic_bytes_per_launch"] = byts / 2
+    roof["launch_gbs"] = {"gate_up": g1_bytes / gemm1_us / 1e3, "down": g2_bytes / gemm2_us / 1e3}
+    roof["mfma_tflops"] = flops / t / 1e12
 
     cpu = None
     if not args.no_cpu_baseline:
