@@ -114,7 +114,8 @@ def moe_expand_layout(x, x_scale, fmt, topk_ids, topk_weights, psum_recv_per_ran
                       num_experts, align, capacity, ex, ex_scale, psum, m_indices,
                       src2dst, row_weight, status, workspace, stream=None):
     """x [rows, >=hidden] fp8 (uint8 view ok), x_scale [rows, >=hidden/128];
-    see moe_expand.h for every argument."""
+    ex_scale [hidden/128, capacity] (K-block-major); see moe_expand.h for
+    every argument."""
     rows, hidden = topk_ids.shape[0], ex.shape[1]
     code = lib().moe_expand_layout(
         _ptr(x), x.stride(0) * x.element_size(), _ptr(x_scale), x_scale.stride(0), _fmt(fmt),
@@ -129,7 +130,8 @@ def moe_expand_layout(x, x_scale, fmt, topk_ids, topk_weights, psum_recv_per_ran
 
 def moe_grouped_gemm_fp8(a, a_scale, fmt, w, w_scale, psum, status, align, out,
                          stream=None):
-    """a [capacity, k] fp8, w [E, n, k] fp8, out [capacity, n] bf16."""
+    """a [capacity, k] fp8, a_scale [k/128, capacity], w [E, n, k] fp8,
+    out [capacity, n] bf16."""
     capacity, k = a.shape
     E, n, _ = w.shape
     code = lib().moe_grouped_gemm_fp8(
@@ -140,7 +142,7 @@ def moe_grouped_gemm_fp8(a, a_scale, fmt, w, w_scale, psum, status, align, out,
 
 def moe_act_quant(gate_up, m_indices, psum, status, num_experts, align, fmt, fold_weight,
                   out, out_scale, stream=None):
-    """gate_up [capacity, 2I] bf16 -> out [capacity, I] fp8, out_scale [capacity, I/128]."""
+    """gate_up [capacity, 2I] bf16 -> out [capacity, I] fp8, out_scale [I/128, capacity]."""
     capacity, two_i = gate_up.shape
     code = lib().moe_act_quant(
         _ptr(gate_up), _ptr(m_indices), _ptr(psum), _ptr(status), capacity, two_i // 2,
@@ -183,7 +185,8 @@ class ExpandedMoE:
         dev = device
         u8 = torch.uint8
         self.ex = torch.empty((cap, H), dtype=u8, device=dev)
-        self.ex_scale = torch.empty((cap, H // 128), dtype=sdt, device=dev)
+        # expanded activation scales are K-block-major: [K/128, capacity]
+        self.ex_scale = torch.empty((H // 128, cap), dtype=sdt, device=dev)
         self.psum = torch.empty(E, dtype=torch.int32, device=dev)
         self.m_indices = torch.empty(cap, dtype=torch.int32, device=dev)
         self.src2dst = torch.empty((rows, topk), dtype=torch.int32, device=dev)
@@ -193,7 +196,7 @@ class ExpandedMoE:
         self.workspace = torch.empty(max(wsb, 256), dtype=u8, device=dev)
         self.gate_up = torch.empty((cap, 2 * self.I), dtype=torch.bfloat16, device=dev)
         self.dq = torch.empty((cap, self.I), dtype=u8, device=dev)
-        self.ds = torch.empty((cap, self.I // 128), dtype=sdt, device=dev)
+        self.ds = torch.empty((self.I // 128, cap), dtype=sdt, device=dev)
         self.down = torch.empty((cap, H), dtype=torch.bfloat16, device=dev)
 
     def layout(self, x, x_scale, topk_ids, topk_weights, psum_recv_per_rank=None,

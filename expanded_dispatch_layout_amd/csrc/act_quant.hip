@@ -42,16 +42,18 @@ __global__ __launch_bounds__(kThreads) void act_quant_kernel(
   const int t = threadIdx.x, lane = t & 63;
   const int64_t nrows = min((int64_t)status[0], capacity);
   const int ngroups = inter / kGroup;
-  const int sbytes = kUe8m0 ? 1 : 4;
   for (int64_t m = blockIdx.x; m < nrows; m += gridDim.x) {
     const int e = m_indices[m];
     if (e < 0 || e >= E) continue;  // uniform per workgroup
     uint8_t* qrow = out + m * inter;
-    uint8_t* srow = out_scale + m * ngroups * sbytes;
+    // out_scale is K-block-major: scale (row m, group g) at g * capacity + m.
     if (m >= psum[e]) {  // alignment pad row: zeros, G is not read
       for (int c = t; c < inter / 16; c += kThreads)
         reinterpret_cast<u32x4*>(qrow)[c] = u32x4{0u, 0u, 0u, 0u};
-      for (int c = t; c < ngroups * sbytes; c += kThreads) srow[c] = 0;
+      for (int g = t; g < ngroups; g += kThreads) {
+        if (kUe8m0) out_scale[g * capacity + m] = 0;
+        else reinterpret_cast<float*>(out_scale)[g * capacity + m] = 0.f;
+      }
       continue;
     }
     const float w = kFold ? fold_w[m] : 1.f;
@@ -100,8 +102,8 @@ __global__ __launch_bounds__(kThreads) void act_quant_kernel(
       *reinterpret_cast<uint2*>(qrow + col) = make_uint2((uint32_t)lo, (uint32_t)hi);
       if ((lane & 15) == 0) {
         const int grp = col / kGroup;
-        if (kUe8m0) srow[grp] = (uint8_t)sbyte;
-        else reinterpret_cast<float*>(srow)[grp] = scale_out;
+        if (kUe8m0) out_scale[grp * capacity + m] = (uint8_t)sbyte;
+        else reinterpret_cast<float*>(out_scale)[grp * capacity + m] = scale_out;
       }
     }
   }

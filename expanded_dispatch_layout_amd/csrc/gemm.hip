@@ -17,14 +17,20 @@
 //    land on one XCD (dispatch is round-robin over the 8 XCDs): that XCD keeps
 //    the group's activations in its L2 while it streams the expert's weights.
 //  - K advances one 128-wide scale block per step = one
-//    v_mfma_scale_f32_16x16x128_f8f6f4 per 16x16 sub-tile.  Four waves in a
-//    2x2 grid, each owning 128 x 64 outputs (8 x 4 MFMA tiles).
-//  - Operands go HBM -> LDS directly (global_load_lds_dwordx4), three LDS
-//    stages, two K steps in flight; each wave waits only for its own oldest
-//    stage (explicit vmcnt) and a bare s_barrier publishes it.  The 16-byte
-//    chunks of every 128-byte row are XOR-swizzled by row (swz), chosen per
-//    lane on the global side, so the 16-row fragment reads are bank-conflict
-//    free.
+//    v_mfma_scale_f32_16x16x128_f8f6f4 per 16x16 sub-tile.  Eight waves (two
+//    per SIMD) in a 4 x 2 grid, each owning 64 x 64 outputs (4 x 4 MFMA tiles).
+//  - Operands go HBM -> LDS directly (global_load_lds_dwordx4) in two rings:
+//    weights (from HBM, long latency) in five slots streamed four K steps
+//    ahead by waves 0-3; activations and their scales (re-read by every N
+//    tile of the group, mostly L2 hits) in 2-4 slots sized to the group,
+//    loaded by waves 4-7.  vmcnt is per wave, so each stream keeps its own
+//    depth.  LDS -> registers runs one step ahead: while the matrix core
+//    works on step k from registers, the wave reads step k+1's fragments.
+//    One bare s_barrier per step publishes the next stage and frees the
+//    slots of the step just moved into registers.
+//    The 16-byte chunks of every 128-byte row are XOR-swizzled by row (swz),
+//    chosen per lane on the global side, so the 16-row fragment reads are
+//    bank-conflict free.
 //  - fp32 scales: each step's MFMA result is promoted into the fp32
 //    accumulator with the row's activation scale times the block's weight
 //    scale (the scales do not factor out of the K sum).
@@ -47,21 +53,45 @@ constexpr int kXcds = 8;       // MI355X: 8 XCDs, workgroups dispatched round-ro
 constexpr int GM = 256;        // rows per work item
 constexpr int BN = 128;
 constexpr int BK = 128;
-constexpr int kStages = 3;
 constexpr int WAVES_N = 2;
+constexpr int WAVES_M = kWaves / WAVES_N;   // 4
 constexpr int WTM = 64, WTN = 64;            // wave tile: 4 x 2 waves cover 256 x 128
 constexpr int FM = WTM / 16, FN = WTN / 16;  // 4 x 4 MFMA tiles per wave
-constexpr int A_BYTES = GM * BK;             // 32 KB
-constexpr int B_BYTES = BN * BK;             // 16 KB
-constexpr int SA_BYTES = GM * 4;             // one scale dword per row
-constexpr int SB_BYTES = 4 * 64 * 4;         // four copies of the block scale
-constexpr int STAGE = A_BYTES + B_BYTES + SA_BYTES + SB_BYTES;
-constexpr int LDS_BYTES = kStages * STAGE;   // 150 KB of the CU's 160 KB
-constexpr int A_LOADS = A_BYTES / (kThreads * 16);  // 16-byte loads per lane per stage
-constexpr int B_LOADS = B_BYTES / (kThreads * 16);
-constexpr int LOADS_PER_STAGE = A_LOADS + B_LOADS + 1;  // + one scale dword
-static_assert(GM * BN * 2 <= LDS_BYTES, "output tile must fit in LDS");
-static_assert(kWaves * 64 == 2 * GM, "scale loads: waves 0-3 A rows, 4-7 block scale");
+// A wave's row tiles are interleaved: M-wave wm owns the 16-row tiles
+// wm, wm + 4, wm + 8, wm + 12, so a group's live rows spread evenly over the
+// M-waves (and over both waves of every SIMD) whatever the group's size.
+constexpr int ROW_TILE_STRIDE = WAVES_M * 16;             // rows between a wave's tiles
+constexpr int A_TILE_STRIDE = ROW_TILE_STRIDE * 128;     // LDS bytes between them
+constexpr int A_BYTES = GM * BK;             // 32 KB: one K block of a full row group
+constexpr int B_BYTES = BN * BK;             // 16 KB: one K block of the N tile's weights
+// Two operand rings.  Weights come from HBM (long latency): kBSlots slots,
+// streamed kBSlots - 1 K steps ahead by waves 0-3.  Activations (re-read by
+// every N tile of the group; the first reader of a K block misses L2): 2..4
+// slots sized to the group, loaded 1..3 steps ahead (with the activation
+// scales) by waves 4-7.  vmcnt is per wave, so each stream keeps its own
+// depth.
+#ifndef GEMM_B_SLOTS
+#define GEMM_B_SLOTS 5
+#endif
+constexpr int kBSlots = GEMM_B_SLOTS;
+constexpr int B_RING = kBSlots * B_BYTES;
+constexpr int A_BASE = B_RING;
+constexpr int A_RING = 2 * A_BYTES;          // two slots of a full group, more if smaller
+constexpr int kMaxASlots = 4;
+constexpr int DATA_BYTES = B_RING + A_RING;  // 144 KB
+constexpr int kScSlots = kMaxASlots + 1;     // the step computed keeps its own
+constexpr int SC_SLOT = GM * 4;              // a step's activation scales (<= 4 B per row)
+constexpr int SC_BASE = DATA_BYTES;
+constexpr int BSC_BYTES = 2048;              // an item's weight block scales, all K blocks
+constexpr int BSC_BASE = SC_BASE + kScSlots * SC_SLOT;
+constexpr int MAX_KB = BSC_BYTES / 4 - 1;    // K / 128 limit (fits BSC_BYTES incl. alignment)
+constexpr int LDS_BYTES = BSC_BASE + BSC_BYTES;  // 150 KB of the CU's 160 KB
+constexpr int kLoadWaves = 4;                // waves per stream: 0-3 weights, 4-7 activations
+constexpr int B_LOADS = B_BYTES / (kLoadWaves * 64 * 16);  // 16-byte loads per lane per stage
+constexpr int A_LOADS = A_BYTES / (kLoadWaves * 64 * 16);  // at most, for a full group
+constexpr int W_LOADS = B_LOADS;             // a weight wave's loads per stage
+static_assert(GM * BN * 2 <= DATA_BYTES, "output tile must fit in LDS");
+static_assert(kWaves == 2 * kLoadWaves && B_LOADS == 4 && A_LOADS == 8, "load split");
 
 // Physical 16-byte chunk of logical chunk c in row r of a [rows][128 B] tile:
 // c ^ key(r), key(r) = (r & 7) ^ ((r >> 3) & 1).  A fragment read serves 16
@@ -81,16 +111,35 @@ __device__ __forceinline__ uint32_t lds_addr(const void* p) {
       (uint32_t)(size_t)(__attribute__((address_space(3))) const void*)p);
 }
 
+// LDS reads by 32-bit LDS address (keeps addresses in single registers and
+// lets constant parts fold into the instruction's offset field).
+template <typename T>
+__device__ __forceinline__ T lds_load(uint32_t addr) {
+  return *reinterpret_cast<const __attribute__((address_space(3))) T*>(addr);
+}
+
 // Direct HBM -> LDS loads.  Issued from inline assembly so the compiler does
 // not treat them as LDS writes that every later LDS read must wait for: the
 // kernel orders them itself (vmcnt waits + s_barrier).  Address = 64-bit
 // scalar base + 32-bit per-lane offset; lane i's data lands at lds + i * size.
+// A wave-uniform pointer, held in scalar registers (the loads' base operand).
+__device__ __forceinline__ const uint8_t* uniform_ptr(const uint8_t* p) {
+  const uint64_t v = (uint64_t)p;
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
+  return (const uint8_t*)(((uint64_t)hi << 32) | lo);
+}
+
 __device__ __forceinline__ void dma16(const uint8_t* base, uint32_t off, uint32_t lds) {
+  base = uniform_ptr(base);                   // wave-uniform by construction
+  lds = __builtin_amdgcn_readfirstlane(lds);  // M0: wave-uniform by construction
   asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(off), "s"(base),
                "s"(lds)
                : "memory");
 }
 __device__ __forceinline__ void dma4(const uint8_t* base, uint32_t off, uint32_t lds) {
+  base = uniform_ptr(base);
+  lds = __builtin_amdgcn_readfirstlane(lds);
   asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dword %0, %1" ::"v"(off), "s"(base),
                "s"(lds)
                : "memory");
@@ -102,100 +151,118 @@ __device__ __forceinline__ void wait_vmcnt() {
   asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
 }
 __device__ __forceinline__ void barrier() { asm volatile("s_barrier" ::: "memory"); }
+// Keep the compiler's scheduler from moving instructions across this point
+// (bounds how far it hoists the next step's fragment reads, and with them
+// the registers they occupy).
+__device__ __forceinline__ void sched_fence() { __builtin_amdgcn_sched_barrier(0); }
+// All of this wave's LDS reads have returned.
+__device__ __forceinline__ void wait_lgkm0() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
 
-// Wait until at most n of this wave's vector-memory operations are
-// outstanding (n is wave-uniform; s_waitcnt takes an immediate).
-__device__ __forceinline__ void wait_vmcnt_rt(int n) {
+// Wait until at most n (0..2 * (A_LOADS + 1)) of this wave's vector-memory
+// operations are outstanding; s_waitcnt takes an immediate.
+__device__ __forceinline__ void wait_vmcnt_upto(int n) {
   switch (n) {
-    case 0: wait_vmcnt<0>(); break;
-    case 1: wait_vmcnt<1>(); break;
-    case 2: wait_vmcnt<2>(); break;
-    case 3: wait_vmcnt<3>(); break;
-    case 4: wait_vmcnt<4>(); break;
-    case 5: wait_vmcnt<5>(); break;
-    case 6: wait_vmcnt<6>(); break;
-    default: wait_vmcnt<LOADS_PER_STAGE>(); break;
+#define MOE_WAIT_CASE(k) \
+  case k:                \
+    wait_vmcnt<k>();     \
+    break;
+    MOE_WAIT_CASE(1) MOE_WAIT_CASE(2) MOE_WAIT_CASE(3) MOE_WAIT_CASE(4) MOE_WAIT_CASE(5)
+    MOE_WAIT_CASE(6) MOE_WAIT_CASE(7) MOE_WAIT_CASE(8) MOE_WAIT_CASE(9) MOE_WAIT_CASE(10)
+    MOE_WAIT_CASE(11) MOE_WAIT_CASE(12) MOE_WAIT_CASE(13) MOE_WAIT_CASE(14) MOE_WAIT_CASE(15)
+    MOE_WAIT_CASE(16) MOE_WAIT_CASE(17) MOE_WAIT_CASE(18)
+#undef MOE_WAIT_CASE
+    default: wait_vmcnt<0>(); break;  // 0, and anything unexpected: wait for all
   }
 }
+static_assert(kMaxASlots - 2 <= 2 && A_LOADS + 1 <= 9, "wait_vmcnt_upto covers 0..18");
 
 struct Item {
   const uint8_t* a;     // first row of the group
   const uint8_t* b;     // first weight row of the N tile
-  const uint8_t* as;    // activation scale array (4-byte aligned base)
-  const uint8_t* bs;    // weight scale array (4-byte aligned base)
-  int64_t as0;          // element index of the group's first row's scales
-  int64_t bs0;          // element index of (expert, N tile, k block 0)
+  const uint8_t* as;    // scale of the group's first row in K block 0
+  int64_t as_kstride;   // bytes from one K block's activation scales to the next
+  const uint8_t* bs;    // aligned word holding the weight scale of (expert, N tile, block 0)
+  int bs_skew;          // byte offset of that scale within the word (UE8M0: 0..3)
   int live;             // rows of the group that hold a slot (1..GM); the
                         // rest of the group is alignment padding
   int KB;               // K / 128
   int K;
   int sbytes;           // 4 (fp32) or 1 (UE8M0)
+  int a_slot_bytes;     // activation slot: live rows rounded to 16, x 128 B
+  int na_slots;         // activation slots that fit (2..kMaxASlots)
 };
 
-// Per-lane byte offsets of one item's loads, fixed over its K steps.
-struct LoadOffsets {
-  uint32_t a[A_LOADS];  // from it.a (+ kb * BK)
-  uint32_t b[B_LOADS];  // from it.b (+ kb * BK)
-  int scale_row;        // activation row whose scale this lane loads
+// Byte offset of this lane's 16-byte chunk of row r in a [rows][K] operand:
+// 8 lanes per 128-byte row segment, chunk order swizzled by row (swz).
+__device__ __forceinline__ uint32_t row_chunk_offset(int r, int lane, int K) {
+  return (uint32_t)r * (uint32_t)K + (uint32_t)((lane & 7) ^ swz_key(r)) * 16u;
+}
+
+// An item's weight block scales for every K block (KB consecutive elements
+// from it.bs + bs_skew), copied into LDS once per item by the last wave as
+// aligned 4-byte words; words past the last one needed re-read it.
+__device__ __forceinline__ void load_item_wscales(const Item& it, uint32_t lds0, int lane) {
+  const int words = (it.bs_skew + it.KB * it.sbytes + 3) >> 2;
+  for (int c = 0; c * 64 < words; ++c) {
+    const int w = c * 64 + lane;
+    dma4(it.bs, (uint32_t)(w < words ? w : words - 1) * 4u, lds0 + BSC_BASE + c * 256);
+  }
+}
+
+// One wave's share of the direct-to-LDS loads of a K step, with the per-lane
+// source offsets computed once per item.  Load j of wave w covers the rows
+// (j * 4 + w) * 8 .. + 8 (8 lanes per 128-byte row), landing at the same
+// offset in the slot.
+//
+// Weights (waves 0-3): the N tile's 128 rows, B_LOADS loads per stage.
+// Activations (waves 4-7): the 8-row blocks that hold live rows (n of them;
+// rows past the live rows inside a loaded block reload the last live row),
+// and for the first of these waves the group's activation scales of the
+// step (one contiguous run: they are K-block-major; lane l brings rows
+// 4l..4l+3, lanes past the live rows re-read the last live row's word).
+struct WaveLoads {
+  uint32_t off[A_LOADS];  // weights use the first B_LOADS
+  uint32_t scale_off;
+  int n;                  // loads per stage (plus one for the scales)
+  bool scales;
+
+  __device__ __forceinline__ void init(const Item& it, int wid, int lane) {
+    const bool wload = wid < kLoadWaves;
+    const int w = wload ? wid : wid - kLoadWaves;
+#pragma unroll
+    for (int j = 0; j < A_LOADS; ++j) {
+      const int r = (j * kLoadWaves + w) * 8 + (lane >> 3);
+      const int rr = wload ? r : min(r, it.live - 1);
+      off[j] = row_chunk_offset(r, lane, it.K) - (uint32_t)(r - rr) * (uint32_t)it.K;
+    }
+    const int blocks = (it.live + 7) >> 3;
+    n = wload ? B_LOADS
+              : max(0, min(A_LOADS, (blocks - w + kLoadWaves - 1) / kLoadWaves));
+    scales = !wload && w == 0;
+    const int l = (it.live - 1) >> 2;
+    scale_off = (uint32_t)(lane < l ? lane : l) * (uint32_t)(4 * it.sbytes);
+  }
+  // Weights of one stage from src (row 0 at K block q) into the slot at lds.
+  __device__ __forceinline__ void weights(const uint8_t* src, uint32_t lds, int w) const {
+#pragma unroll
+    for (int j = 0; j < B_LOADS; ++j) dma16(src, off[j], lds + (j * kLoadWaves + w) * 1024);
+  }
+  // Activations (and scales) of one stage.
+  __device__ __forceinline__ void acts(const uint8_t* src, uint32_t lds, int w,
+                                       const uint8_t* ssrc, uint32_t slds, bool f32) const {
+#pragma unroll
+    for (int j = 0; j < A_LOADS; ++j)
+      if (j < n) dma16(src, off[j], lds + (j * kLoadWaves + w) * 1024);
+    if (scales) {
+      if (f32) dma16(ssrc, scale_off, slds);
+      else dma4(ssrc, scale_off, slds);
+    }
+  }
 };
-
-__device__ __forceinline__ LoadOffsets load_offsets(const Item& it, int lane, int wid) {
-  LoadOffsets o;
-#pragma unroll
-  for (int j = 0; j < A_LOADS; ++j) {
-    const int r = (wid * A_LOADS + j) * 8 + (lane >> 3);
-    const int c = (lane & 7) ^ swz_key(r);
-    const int rr = r < it.live ? r : it.live - 1;  // reload the last live row
-    o.a[j] = (uint32_t)rr * (uint32_t)it.K + (uint32_t)c * 16u;
-  }
-#pragma unroll
-  for (int j = 0; j < B_LOADS; ++j) {
-    const int r = (wid * B_LOADS + j) * 8 + (lane >> 3);
-    const int c = (lane & 7) ^ swz_key(r);
-    o.b[j] = (uint32_t)r * (uint32_t)it.K + (uint32_t)c * 16u;
-  }
-  const int r = wid * 64 + lane;
-  o.scale_row = r < it.live ? r : it.live - 1;
-  return o;
-}
-
-// Issue the direct-to-LDS loads of K step kb into `stage`.  A wave skips the
-// activation loads whose 8 rows are all alignment padding (rows past the
-// live rows inside a loaded 8-row block reload the last live row); the number
-// of loads a wave issues per stage is the same for every stage of an item
-// (stage_loads), which is what its vmcnt waits count on.
-__device__ __forceinline__ void issue_stage(const Item& it, const LoadOffsets& o, uint8_t* stage,
-                                            int kb, int wid) {
-#ifdef PROBE_NO_LOADS
-  return;
-#endif
-  const uint8_t* abase = it.a + kb * BK;
-  const uint8_t* bbase = it.b + kb * BK;
-#pragma unroll
-  for (int j = 0; j < A_LOADS; ++j) {
-    const int base = (wid * A_LOADS + j) * 8;  // 8 rows per wave instruction
-    if (base >= it.live) break;                // only padding rows: not loaded
-    dma16(abase, o.a[j], lds_addr(stage + base * 128));
-  }
-#pragma unroll
-  for (int j = 0; j < B_LOADS; ++j) {
-    const int base = (wid * B_LOADS + j) * 8;
-    dma16(bbase, o.b[j], lds_addr(stage + A_BYTES + base * 128));
-  }
-  // Scales: the aligned dword holding each element (UE8M0 bytes are picked
-  // out of it when used).  Waves 0-3: one activation row each lane; waves
-  // 4-7: a copy of the weight block scale.
-  if (wid < 4) {
-    const int64_t off = (it.as0 + (int64_t)o.scale_row * it.KB + kb) * it.sbytes;
-    dma4(it.as, (uint32_t)(off & ~(int64_t)3), lds_addr(stage + A_BYTES + B_BYTES + wid * 256));
-  } else {
-    const int64_t boff = ((it.bs0 + kb) * it.sbytes) & ~(int64_t)3;
-    dma4(it.bs + boff, 0u, lds_addr(stage + A_BYTES + B_BYTES + SA_BYTES + (wid - 4) * 256));
-  }
-}
 
 // Per-lane LDS byte offsets (within a stage) of the two 16-byte halves of
-// this lane's A and B fragments for row/column tile 0; tile i adds i * 2048.
+// this lane's A and B fragments for row/column tile 0; row tile i adds
+// i * A_TILE_STRIDE, column tile j adds j * 2048.
 struct FragOffsets {
   int a_lo, a_hi, b_lo, b_hi, s_row;
 };
@@ -203,19 +270,18 @@ struct FragOffsets {
 __device__ __forceinline__ FragOffsets frag_offsets(int lane, int wm, int wn) {
   const int frow = lane & 15, fk = (lane >> 4) * 2;
   FragOffsets f;
-  const int ra = wm * WTM + frow, rb = wn * WTN + frow;
+  const int ra = wm * 16 + frow, rb = wn * WTN + frow;
   f.a_lo = swz(ra, fk);
   f.a_hi = swz(ra, fk + 1);
-  f.b_lo = A_BYTES + swz(rb, fk);
-  f.b_hi = A_BYTES + swz(rb, fk + 1);
-  f.s_row = wm * WTM + (lane >> 4) * 4;  // first output row of this lane
+  f.b_lo = swz(rb, fk);  // within a weight slot
+  f.b_hi = swz(rb, fk + 1);
+  f.s_row = wm * 16 + (lane >> 4) * 4;  // first output row of this lane (row tile 0)
   return f;
 }
 
-__device__ __forceinline__ v8i frag2(const uint8_t* stage, int lo_off, int hi_off) {
-  typedef unsigned int u4 __attribute__((ext_vector_type(4)));
-  const u4 lo = *reinterpret_cast<const u4*>(stage + lo_off);
-  const u4 hi = *reinterpret_cast<const u4*>(stage + hi_off);
+__device__ __forceinline__ v8i frag2(uint32_t base, int lo_off, int hi_off) {
+  const u32x4 lo = lds_load<u32x4>(base + lo_off);
+  const u32x4 hi = lds_load<u32x4>(base + hi_off);
   return v8i{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3], (int)hi[0], (int)hi[1], (int)hi[2],
              (int)hi[3]};
 }
@@ -225,78 +291,165 @@ __device__ __forceinline__ v4f mfma_plain(const v8i& a, const v8i& b) {
                                                           127, 0, 127);
 }
 
-// NFM: how many of the wave's four 16-row tiles hold live rows.
-template <bool kUe8m0, int NFM>
-__device__ __forceinline__ void compute_stage(const uint8_t* stage, v4f (&acc)[FM][FN],
-                                              const Item& it, const FragOffsets& fo, int kb,
-                                              int lane, int nfm_rt) {
-#ifdef PROBE_NO_COMPUTE
-  return;
-#endif
-  const uint32_t* ssa = reinterpret_cast<const uint32_t*>(stage + A_BYTES + B_BYTES);
-  const uint32_t* ssb = reinterpret_cast<const uint32_t*>(stage + A_BYTES + B_BYTES + SA_BYTES);
-  v8i bf[FN];
-#pragma unroll
-  for (int j = 0; j < FN; ++j) bf[j] = frag2(stage + j * 2048, fo.b_lo, fo.b_hi);
+// One K step from registers: a[0..NFM) x b[0..FN) of step kb; the step's
+// activation scales come from scale slot `sc` (read first, so that waiting
+// for them never waits for the reads issued after them) and its weight
+// block scale from `bsc` (the item's scales at K block kb).  With kNext, the
+// fragments of step kb+1 replace the old ones as soon as the MFMAs that read
+// them are issued: A row tile i after MFMA (i, FN-1), B column tile j after
+// MFMA (NFM-1, j), from slots next_a / next_b.  NFM: how many of the wave's
+// four 16-row tiles hold live rows.
+template <bool kUe8m0, int NFM, bool kNext>
+__device__ __forceinline__ void step(v8i (&a)[FM], v8i (&b)[FN], v4f (&acc)[FM][FN],
+                                     uint32_t next_a, uint32_t next_b, uint32_t sc, uint32_t bsc,
+                                     const Item& it, const FragOffsets& fo, int kb, int lane) {
+  constexpr int M = NFM * FN;  // MFMAs of this step
+  auto refresh = [&](int t) {  // after MFMA t
+    if constexpr (kNext) {
+      const int i = t / FN, j = t % FN;
+      if (i == NFM - 1) b[j] = frag2(next_b + j * 2048, fo.b_lo, fo.b_hi);
+      if (j == FN - 1) a[i] = frag2(next_a + i * A_TILE_STRIDE, fo.a_lo, fo.a_hi);
+    }
+  };
   if constexpr (kUe8m0) {
-    const int sbyte = (int)((ssb[0] >> (8 * (int)((it.bs0 + kb) & 3))) & 0xffu);
     const int arow = fo.s_row - (lane >> 4) * 4 + (lane & 15);  // this lane's A row
+    const int bpos = it.bs_skew + kb;
+    const uint32_t sbw = lds_load<uint32_t>(bsc + (bpos & ~3));
+    uint32_t aw[NFM];  // row r's exponent byte is byte r of the slot
 #pragma unroll
-    for (int i = 0; i < FM; ++i) {
-      if (i >= nfm_rt) break;  // uniform per wave
-      const int r = arow + i * 16;
-      const v8i af = frag2(stage + i * 2048, fo.a_lo, fo.a_hi);
-      const int apos = (int)((it.as0 + (int64_t)r * it.KB + kb) & 3);
-      const int abyte = (int)((ssa[r] >> (8 * apos)) & 0xffu);
-#pragma unroll
-      for (int j = 0; j < FN; ++j)
-        acc[i][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(af, bf[j], acc[i][j], 0, 0,
-                                                                     0, abyte, 0, sbyte);
-    }
-  } else {
-    // Software pipeline: the MFMAs of row tile i+1 are issued before the
-    // promotion of row tile i, so the matrix core always has work queued
-    // while the VALU scales and accumulates.
-    const float sbv = __uint_as_float(ssb[0]);
-    v4f p[2][FN];
-    if constexpr (NFM > 0) {
-      const v8i af = frag2(stage, fo.a_lo, fo.a_hi);
-#pragma unroll
-      for (int j = 0; j < FN; ++j) p[0][j] = mfma_plain(af, bf[j]);
-    }
+    for (int i = 0; i < NFM; ++i)
+      aw[i] = lds_load<uint32_t>(sc + ((arow + i * ROW_TILE_STRIDE) & ~3));
+    sched_fence();
+    const int sbyte = (int)((sbw >> (8 * (bpos & 3))) & 0xffu);
 #pragma unroll
     for (int i = 0; i < NFM; ++i) {
-      if (i + 1 < NFM) {
-        const v8i af = frag2(stage + (i + 1) * 2048, fo.a_lo, fo.a_hi);
+      const int abyte = (int)((aw[i] >> (8 * ((arow + i * ROW_TILE_STRIDE) & 3))) & 0xffu);
 #pragma unroll
-        for (int j = 0; j < FN; ++j) p[(i + 1) & 1][j] = mfma_plain(af, bf[j]);
+      for (int j = 0; j < FN; ++j) {
+        acc[i][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a[i], b[j], acc[i][j], 0, 0,
+                                                                     0, abyte, 0, sbyte);
+        refresh(i * FN + j);
       }
-      float sc[4];
+      sched_fence();
+    }
+  } else {
+    // fp32 scales: each 16x16 product is promoted into the accumulator
+    // (acc += P * sa * sb) while the matrix core runs the next product; two
+    // product registers in rotation.
+    const float sbv = lds_load<float>(bsc + kb * 4);
+    v4f s4[NFM];
 #pragma unroll
-      for (int q = 0; q < 4; ++q) sc[q] = __uint_as_float(ssa[fo.s_row + i * 16 + q]) * sbv;
+    for (int i = 0; i < NFM; ++i)
+      s4[i] = lds_load<v4f>(sc + (fo.s_row + i * ROW_TILE_STRIDE) * 4);
+    sched_fence();
+    v4f p[2];
+    v4f scl;
 #pragma unroll
-      for (int j = 0; j < FN; ++j)
+    for (int t = 0; t <= M; ++t) {
+      if (t < M) p[t & 1] = mfma_plain(a[t / FN], b[t % FN]);
+      if (t > 0) {
+        const int u = t - 1, i = u / FN, j = u % FN;
+        if (j == 0) {
 #pragma unroll
-        for (int q = 0; q < 4; ++q) acc[i][j][q] += p[i & 1][j][q] * sc[q];
+          for (int q = 0; q < 4; ++q) scl[q] = s4[i][q] * sbv;
+        }
+#pragma unroll
+        for (int q = 0; q < 4; ++q) acc[i][j][q] += p[u & 1][q] * scl[q];
+      }
+      if (t < M) refresh(t);
+      sched_fence();
     }
   }
 }
 
-// The K loop of one item: wait for stage kb (this wave's loads; the barrier
-// makes every wave's visible and retires the stage read one step ago), refill
-// that older stage with step kb+2, compute on stage kb.
+// The K loop of one item.  Each wave feeds one stream: weights (waves 0-3,
+// kBSlots - 1 stages ahead) or activations + scales (waves 4-7, na_slots - 1
+// stages ahead).  Step kb: wait for this wave's loads of stage kb+1 and for its
+// reads of step kb's fragments; barrier (stage kb+1 is now visible to every
+// wave, and every wave holds step kb's fragments in registers, so the slots
+// of stage kb are free); refill them with the next stage of the stream;
+// compute step kb from registers while reading step kb+1's fragments.
 template <bool kUe8m0, int NFM>
-__device__ __forceinline__ void kloop(uint8_t* lds, v4f (&acc)[FM][FN], const Item& it,
-                                      const LoadOffsets& lo_, const FragOffsets& fo, int lane,
-                                      int wid, int nfm, int stage_loads) {
-  for (int kb = 0; kb < it.KB; ++kb) {
-    if (kb + 1 < it.KB) wait_vmcnt_rt(stage_loads);
-    else wait_vmcnt<0>();
-    barrier();
-    if (kb + 2 < it.KB) issue_stage(it, lo_, lds + ((kb + 2) % kStages) * STAGE, kb + 2, wid);
-    if (NFM > 0 || (kUe8m0 && nfm > 0))
-      compute_stage<kUe8m0, NFM>(lds + (kb % kStages) * STAGE, acc, it, fo, kb, lane, nfm);
+__device__ __forceinline__ void kloop(uint32_t lds0, v4f (&acc)[FM][FN], const Item& it,
+                                      const WaveLoads& wl, const FragOffsets& fo, int lane,
+                                      int wid) {
+  const int KB = it.KB;
+  const bool wload = wid < kLoadWaves;
+  const int w = wload ? wid : wid - kLoadWaves;
+  const int D = wload ? kBSlots : it.na_slots;   // stream depth (slots)
+  const int nl = wl.n + (wl.scales ? 1 : 0);     // activation loads per stage
+  const uint32_t a_end = lds0 + A_BASE + (uint32_t)(it.na_slots * it.a_slot_bytes);
+  // Wait for this wave's stage (issued - 1 - ahead): at most `ahead` later
+  // stages of its stream stay in flight.
+  auto wait_stage = [&](int ahead) {
+    if (wload) {
+      static_assert(kBSlots == 5, "weight-stream waits assume five slots");
+      if (ahead >= 3) wait_vmcnt<3 * W_LOADS>();
+      else if (ahead == 2) wait_vmcnt<2 * W_LOADS>();
+      else if (ahead == 1) wait_vmcnt<W_LOADS>();
+      else wait_vmcnt<0>();
+    } else {
+      wait_vmcnt_upto(ahead * nl);
+    }
+  };
+  // Stream state: source pointers and destination slots of the next stage to
+  // load, advanced one stage per issue.
+  const uint8_t* src = wload ? it.b : it.a;
+  const uint8_t* ssrc = it.as;
+  uint32_t bdst = lds0, adst = lds0 + A_BASE, sdst = lds0 + SC_BASE;
+  auto issue = [&]() {
+    if (wload) {
+      wl.weights(src, bdst, w);
+      bdst = bdst + B_BYTES == lds0 + B_RING ? lds0 : bdst + B_BYTES;
+    } else {
+      wl.acts(src, adst, w, ssrc, sdst, !kUe8m0);
+      adst = adst + it.a_slot_bytes == a_end ? lds0 + A_BASE : adst + it.a_slot_bytes;
+      sdst = sdst + SC_SLOT == lds0 + SC_BASE + kScSlots * SC_SLOT ? lds0 + SC_BASE
+                                                                    : sdst + SC_SLOT;
+      ssrc += it.as_kstride;
+    }
+    src += BK;
+  };
+  // Read-side slots of stage kb+1, and the scale slot of stage kb.
+  uint32_t rb = lds0 + B_BYTES, ra = lds0 + A_BASE + it.a_slot_bytes, rs = lds0 + SC_BASE;
+  const uint32_t bsc = lds0 + BSC_BASE;
+
+  // The item's weight block scales: issued before this wave's stage 0, so
+  // the prologue's wait for stage 0 covers them too (loads complete in order).
+  if (wid == kWaves - 1) load_item_wscales(it, lds0, lane);
+  // Prologue: stages 0..D-2 of the stream, wait for stage 0 with the rest
+  // in flight; after the barrier, read stage 0's fragments and issue the
+  // stream's next stage into the last free slot.
+  const int pre = min(D - 1, KB);
+  for (int q = 0; q < pre; ++q) issue();
+  wait_stage(pre - 1);
+  barrier();
+  v8i a[FM], b[FN];
+  if constexpr (NFM > 0) {
+#pragma unroll
+    for (int j = 0; j < FN; ++j) b[j] = frag2(lds0 + j * 2048, fo.b_lo, fo.b_hi);
+#pragma unroll
+    for (int i = 0; i < NFM; ++i)
+      a[i] = frag2(lds0 + A_BASE + i * A_TILE_STRIDE, fo.a_lo, fo.a_hi);
   }
+  int issued = pre;  // stages of this wave's stream issued so far
+  if (issued < KB) { issue(); ++issued; }
+  for (int kb = 0; kb + 1 < KB; ++kb) {
+    // Stage kb+1 must have landed; the later stages issued may stay in flight.
+    wait_stage(issued - (kb + 2));
+    wait_lgkm0();
+    barrier();
+    if (issued < KB) { issue(); ++issued; }  // into the slots stage kb had
+    if constexpr (NFM > 0)
+      step<kUe8m0, NFM, true>(a, b, acc, ra, rb, rs, bsc, it, fo, kb, lane);
+    rb = rb + B_BYTES == lds0 + B_RING ? lds0 : rb + B_BYTES;
+    ra = ra + it.a_slot_bytes == a_end ? lds0 + A_BASE : ra + it.a_slot_bytes;
+    rs = rs + SC_SLOT == lds0 + SC_BASE + kScSlots * SC_SLOT ? lds0 + SC_BASE : rs + SC_SLOT;
+  }
+  // Last step: nothing left to read ahead or load; its scales were published
+  // by the previous barrier (or the prologue's).
+  if constexpr (NFM > 0)
+    step<kUe8m0, NFM, false>(a, b, acc, 0u, 0u, rs, bsc, it, fo, KB - 1, lane);
 }
 
 template <bool kUe8m0>
@@ -307,9 +460,11 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(
     int K, int E, int align, uint16_t* __restrict__ out) {
   __shared__ __attribute__((aligned(16))) uint8_t lds[LDS_BYTES];
   __shared__ int gp[MOE_MAX_EXPERTS + 1];  // prefix of row groups per expert
-  const int t = threadIdx.x, lane = t & 63, wid = t >> 6;
+  const int t = threadIdx.x, lane = t & 63;
+  const int wid = __builtin_amdgcn_readfirstlane(t >> 6);  // uniform per wave
   const int wm = wid / WAVES_N, wn = wid % WAVES_N;
   const FragOffsets fo = frag_offsets(lane, wm, wn);
+  const uint32_t lds0 = lds_addr(lds);
   const int64_t nrows = min((int64_t)status[0], capacity);
   const int sbytes = kUe8m0 ? 1 : 4;
   const int KB = K / BK, NT = N / BN;
@@ -355,16 +510,20 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(
     it.K = K;
     it.KB = KB;
     it.sbytes = sbytes;
+    it.a_slot_bytes = (((int)live + 15) & ~15) * BK;
+    it.na_slots = min(kMaxASlots, A_RING / it.a_slot_bytes);  // >= 2
     it.a = a + m0 * K;
     it.b = w + ((int64_t)e * N + (int64_t)nt * BN) * K;
-    it.as = a_scale;
-    it.bs = w_scale;
-    it.as0 = m0 * KB;
-    it.bs0 = ((int64_t)e * NT + nt) * KB;
+    it.as = a_scale + m0 * sbytes;
+    it.as_kstride = capacity * sbytes;
+    {
+      const int64_t b0 = ((int64_t)e * NT + nt) * KB * sbytes;  // byte of block 0's scale
+      it.bs = w_scale + (b0 & ~(int64_t)3);
+      it.bs_skew = (int)(b0 & 3);
+    }
     // Live 16-row MFMA tiles of this wave, and the loads it issues per stage.
-    const int nfm = (int)max(0, min(FM, (it.live - wm * WTM + 15) / 16));
-    const int na = (int)max(0, min(A_LOADS, (it.live - wid * A_LOADS * 8 + 7) / 8));
-    const int stage_loads = na + B_LOADS + 1;
+    const int nfm = (int)max(0, min(FM, (it.live - wm * 16 + ROW_TILE_STRIDE - 1) /
+                                            ROW_TILE_STRIDE));
 
     v4f acc[FM][FN];
 #pragma unroll
@@ -372,22 +531,18 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(
 #pragma unroll
       for (int j = 0; j < FN; ++j) acc[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
 
-    const LoadOffsets lo_ = load_offsets(it, lane, wid);
+    WaveLoads wl;
+    wl.init(it, wid, lane);
     wait_vmcnt<0>();  // nothing older (previous item's stores) left in flight
-    issue_stage(it, lo_, lds, 0, wid);
-    if (KB > 1) issue_stage(it, lo_, lds + STAGE, 1, wid);
-    if constexpr (kUe8m0) {
-      kloop<true, FM>(lds, acc, it, lo_, fo, lane, wid, nfm, stage_loads);
-    } else {
-      switch (nfm) {  // uniform per wave; one K loop per live-tile count
-        case 4: kloop<false, 4>(lds, acc, it, lo_, fo, lane, wid, 4, stage_loads); break;
-        case 3: kloop<false, 3>(lds, acc, it, lo_, fo, lane, wid, 3, stage_loads); break;
-        case 2: kloop<false, 2>(lds, acc, it, lo_, fo, lane, wid, 2, stage_loads); break;
-        case 1: kloop<false, 1>(lds, acc, it, lo_, fo, lane, wid, 1, stage_loads); break;
-        default: kloop<false, 0>(lds, acc, it, lo_, fo, lane, wid, 0, stage_loads); break;
-      }
+    switch (nfm) {  // uniform per wave; one K loop per live-tile count
+      case 4: kloop<kUe8m0, 4>(lds0, acc, it, wl, fo, lane, wid); break;
+      case 3: kloop<kUe8m0, 3>(lds0, acc, it, wl, fo, lane, wid); break;
+      case 2: kloop<kUe8m0, 2>(lds0, acc, it, wl, fo, lane, wid); break;
+      case 1: kloop<kUe8m0, 1>(lds0, acc, it, wl, fo, lane, wid); break;
+      default: kloop<kUe8m0, 0>(lds0, acc, it, wl, fo, lane, wid); break;
     }
-    barrier();  // every wave is done reading the stages
+    wait_lgkm0();
+    barrier();  // every wave is done reading the slots
 
     // Epilogue: bf16 tile through LDS, then 16-byte stores of the live rows.
     uint16_t* ct = reinterpret_cast<uint16_t*>(lds);
@@ -397,7 +552,7 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(
       for (int j = 0; j < FN; ++j)
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
-          const int r = wm * WTM + i * 16 + (lane >> 4) * 4 + q;
+          const int r = wm * 16 + i * ROW_TILE_STRIDE + (lane >> 4) * 4 + q;
           const int c = wn * WTN + j * 16 + (lane & 15);
           ct[r * BN + c] = f32_to_bf16_rne(acc[i][j][q]);
         }
@@ -444,8 +599,9 @@ extern "C" moe_status moe_grouped_gemm_fp8(const void* a, const void* a_scale, m
   if (fmt != MOE_SCALE_F32 && fmt != MOE_SCALE_UE8M0) return MOE_ERR_UNSUPPORTED;
   if (!psum || !status || !w || !w_scale) return MOE_ERR_NULL;
   if (capacity > 0 && (!a || !a_scale || !out)) return MOE_ERR_NULL;
+  if (k / BK > MAX_KB) return MOE_ERR_UNSUPPORTED;
   if (((uintptr_t)a % 16) || ((uintptr_t)w % 16) || ((uintptr_t)out % 16) ||
-      ((uintptr_t)a_scale % 4) || ((uintptr_t)w_scale % 4))
+      ((uintptr_t)a_scale % (fmt == MOE_SCALE_F32 ? 16 : 4)) || ((uintptr_t)w_scale % 4))
     return MOE_ERR_ALIGNMENT;
   if (capacity == 0) return MOE_OK;
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);

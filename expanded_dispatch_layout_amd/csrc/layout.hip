@@ -260,11 +260,13 @@ __global__ __launch_bounds__(kScatterThreads) void expand_scatter_kernel(
         else
           sb = (x_scale + r * x_scale_stride_bytes)[c];
       }
+      // ex_scale is K-block-major: scale (row dk, block c) at c * capacity + dk.
       for (uint64_t mm = mask; mm; mm &= mm - 1) {
         const int dk = __shfl(d, __builtin_ctzll(mm), 64);
         if (c < nsc) {
-          if (scale_bytes == 4) reinterpret_cast<float*>(ex_scale + (int64_t)dk * nsc * 4)[c] = sf;
-          else (ex_scale + (int64_t)dk * nsc)[c] = sb;
+          const int64_t at = (int64_t)c * capacity + dk;
+          if (scale_bytes == 4) reinterpret_cast<float*>(ex_scale)[at] = sf;
+          else ex_scale[at] = sb;
         }
       }
     }
@@ -286,7 +288,11 @@ __global__ __launch_bounds__(kScatterThreads) void expand_scatter_kernel(
     u32x4* dst = reinterpret_cast<u32x4*>(ex + row * hidden);
     const u32x4 z = {0u, 0u, 0u, 0u};
     for (int c = lane; c < nch; c += 64) dst[c] = z;
-    for (int c = lane; c < nsc * scale_bytes; c += 64) ex_scale[row * nsc * scale_bytes + c] = 0;
+    for (int c = lane; c < nsc; c += 64) {
+      const int64_t at = (int64_t)c * capacity + row;
+      if (scale_bytes == 4) reinterpret_cast<float*>(ex_scale)[at] = 0.f;
+      else ex_scale[at] = 0;
+    }
     if (lane == 0 && row_weight) row_weight[row] = 0.f;
   }
 }

@@ -53,8 +53,15 @@
  *  - fp8 is OCP E4M3 ("fn": bias 7, max 448, no infinities).  bf16 buffers
  *    hold raw 16-bit patterns.  fp32 scales are IEEE float; UE8M0 scales are
  *    one unsigned exponent byte per group, value 2^(b-127).
- *  - Activation scales are row-major [rows, K/128] (one per 1x128 group);
- *    weight scales are [E, N/128, K/128] (one per 128x128 block).
+ *  - Scales: one per 1x128 activation group, one per 128x128 weight block.
+ *    The received rows' x_scale is row-major [rows, K/128].  The expanded
+ *    activation scales that moe_expand_layout and moe_act_quant write and
+ *    moe_grouped_gemm_fp8 reads are K-block-major ("MN-major")
+ *    [K/128, capacity]: the scale of expanded row m, K block b sits at
+ *    b * capacity + m, so one K block's scales for consecutive rows are one
+ *    contiguous run (the GEMM of [P3 _run_contiguous_gemm] likewise takes its
+ *    activation scales transposed: TMA-aligned, or mn-major under UE8M0).
+ *    Weight scales are [E, N/128, K/128].
  *  - Calls are stateless and reentrant; calls that share output buffers
  *    must be ordered by the caller's streams.
  */
@@ -130,7 +137,8 @@ size_t moe_expand_workspace_bytes(int64_t rows, int topk, int num_experts);
  *   x_stride % 16 == 0 and x 16-byte aligned.
  * Outputs (device, caller-allocated):
  *   ex             [capacity, hidden] fp8 expanded rows
- *   ex_scale       [capacity, hidden/128] scales (same format as x_scale)
+ *   ex_scale       [hidden/128, capacity] K-block-major scales (same
+ *                  format as x_scale): row m, block b at b * capacity + m
  *   psum           [num_experts] int32, psum[e] = align(psum[e-1]) + count[e]
  *   m_indices      [capacity] int32: expert of each expanded row, alignment
  *                  pads included; -1 from the total to the capacity
@@ -162,7 +170,8 @@ moe_status moe_expand_layout(
  * Contiguous grouped fp8 GEMM, "NT": out[m, :] = A[m, :] . W[e]^T for every
  * expanded row m of expert e [P3 _run_contiguous_gemm; P1 Core].
  *
- *   a        [capacity, k] fp8 (row stride k), a_scale [capacity, k/128]
+ *   a        [capacity, k] fp8 (row stride k), a_scale [k/128, capacity]
+ *            K-block-major (row m, block b at b * capacity + m)
  *   w        [num_experts, n, k] fp8 (k contiguous), w_scale
  *            [num_experts, n/128, k/128]; a_scale and w_scale in `fmt`
  *   psum, status  as written by moe_expand_layout
@@ -176,8 +185,11 @@ moe_status moe_expand_layout(
  * accumulated in fp32 (UE8M0: the exponents are applied by the matrix
  * cores).  Row groups made only of alignment padding (rows >= psum[e]) may
  * be skipped and left unwritten; rows past the total are never written.
- * Sizes: n % 128 == 0, k % 128 == 0, align as for the layout, capacity a
- * multiple of align; a, w, out 16-byte aligned, scales 4-byte aligned.
+ * Sizes: n % 128 == 0, k % 128 == 0, k / 128 <= 511 (else
+ * MOE_ERR_UNSUPPORTED), align as for the layout, capacity a multiple of
+ * align.  Alignment: a, w, out 16 bytes; a_scale 16 bytes (fp32) or 4
+ * (UE8M0); w_scale 4 bytes.  UE8M0 scale arrays are read in aligned 4-byte
+ * words, so their allocations must extend to a multiple of 4 bytes.
  */
 moe_status moe_grouped_gemm_fp8(
     const void* a, const void* a_scale, moe_scale_fmt fmt,
@@ -195,7 +207,8 @@ moe_status moe_grouped_gemm_fp8(
  *   m_indices, psum, status  as written by moe_expand_layout
  *   fold_weight  [capacity] fp32 (the layout's row_weight) or NULL.  Only
  *                with MOE_SCALE_F32 (UE8M0 + fold -> MOE_ERR_UNSUPPORTED).
- *   out       [capacity, inter] fp8; out_scale [capacity, inter/128] in fmt
+ *   out       [capacity, inter] fp8; out_scale [inter/128, capacity] in fmt,
+ *             K-block-major (row m, group g at g * capacity + m)
  * For each live row m (m < min(status[0], capacity), m < psum[e]):
  *   y = g / (1 + exp(-g)) * u in fp32; per group amax = max(|y|, 1e-10);
  *   F32:   s = amax / 448, q = fp8_rne(y * (448 / amax)), s *= fold_weight[m]

@@ -104,6 +104,9 @@ def test_gemm_rejects_bad_arguments():
     assert call(fmt=3) == M.MOE_ERR_UNSUPPORTED
     assert call(psum=None) == M.MOE_ERR_NULL
     assert call(as_=FAKE + 2) == M.MOE_ERR_ALIGNMENT
+    assert call(as_=FAKE + 4) == M.MOE_ERR_ALIGNMENT        # fp32 scales: 16 bytes
+    assert call(as_=FAKE + 4, fmt=1, cap=0) == M.MOE_OK     # UE8M0 scales: 4 bytes
+    assert call(k=512 * 128) == M.MOE_ERR_UNSUPPORTED       # item scales fit LDS
     assert call(a=MIS) == M.MOE_ERR_ALIGNMENT
     assert call(cap=0) == M.MOE_OK                  # nothing to do, nothing launched
 

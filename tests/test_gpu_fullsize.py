@@ -54,7 +54,7 @@ def check_layout(name, inp, mod):
     assert np.array_equal(src, lay["src2dst"])
     n = lay["total"]
     ex = mod.ex[:n + 8].cpu().numpy()
-    exs = mod.ex_scale[:n].cpu().numpy()
+    exs = mod.ex_scale.t()[:n].contiguous().cpu().numpy()   # stored K-block-major
     rw = mod.row_weight[:n].cpu().numpy()
     live = src >= 0
     rr, kk = np.nonzero(live)

@@ -119,6 +119,12 @@ SMALL = [
 IDS = [f"{n}-{'-'.join(f'{k}{v}' for k, v in o.items())}" for n, o in SMALL]
 
 
+def rows_major(scales):
+    """Expanded scales are K-block-major [K/128, capacity] on the device; the
+    oracle keeps them per row [capacity, K/128]."""
+    return scales.t().contiguous().cpu().numpy()
+
+
 def check_layout(mod, inp):
     R, T = inp["ids"].shape
     E = inp["w13_q"].shape[0]
@@ -134,7 +140,7 @@ def check_layout(mod, inp):
     ex = mod.ex.cpu().numpy()
     assert np.array_equal(ex[:n], ref["ex"])
     assert np.all(ex[n:] == SENT)                         # past the total: untouched
-    assert np.array_equal(mod.ex_scale.cpu().numpy()[:n].view(np.uint8),
+    assert np.array_equal(rows_major(mod.ex_scale)[:n].view(np.uint8),
                           np.ascontiguousarray(ref["ex_scale"]).view(np.uint8))
     assert np.array_equal(mod.row_weight.cpu().numpy()[:n].view(np.uint32),
                           ref["row_weight"].view(np.uint32))
@@ -207,7 +213,7 @@ def test_stages_against_oracle(name, over):
                     mod.ds)
     torch.cuda.synchronize()
     dq = mod.dq.cpu().numpy()[:n]
-    ds = mod.ds.cpu().numpy()[:n]
+    ds = rows_major(mod.ds)[:n]
     assert np.array_equal(dq[~live], L["dq"][~live]) and not ds[~live].any()
     diff = dq[live] != L["dq"][live]
     assert diff.mean() < 1e-3
@@ -221,7 +227,7 @@ def test_stages_against_oracle(name, over):
         assert np.array_equal(ds[live], L["ds"][live])
     # GEMM2 on the oracle's dq/ds
     mod.dq[:n] = torch.from_numpy(L["dq"]).cuda()
-    mod.ds[:n] = torch.from_numpy(np.ascontiguousarray(L["ds"])).cuda()
+    mod.ds.t()[:n] = torch.from_numpy(np.ascontiguousarray(L["ds"])).cuda()
     M.moe_grouped_gemm_fp8(mod.dq, mod.ds, fmt, mod.w2, mod.w2_scale, mod.psum, mod.status,
                            align, mod.down)
     torch.cuda.synchronize()
