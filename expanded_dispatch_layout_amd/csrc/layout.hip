@@ -8,37 +8,46 @@
 // vLLM PR 54109 PaddedStandard (Motivation/Design: -1 slots, device-side
 // real/padding boundary, zeroed alignment gaps).
 //
-// Three kernels on one stream:
-//  1. count   one thread per received row; order-free per-expert counts of
-//             every 16-row group (LDS atomics) -> workspace.
-//  2. scan    one workgroup: per-expert exclusive scan over the groups (one
-//             wave per expert column), then the expert starts as the
-//             exclusive scan of the aligned counts (every start is aligned,
-//             so start[e] = sum of align(count) over e' < e), psum, total,
+// Three kernels on one stream (two when the block table is small: every
+// scatter workgroup then scans it itself):
+//  1. count   one thread per received row; a block covers G 16-row groups
+//             (G = 64 when the per-group table fits LDS).  Order-free
+//             per-expert counts of every group (LDS atomics), then, per
+//             expert, the exclusive offset of each group within the block
+//             and the block's total -> workspace.
+//  2. scan    one workgroup: per-expert exclusive scan over the block totals
+//             (a few per expert), then the expert starts as the exclusive
+//             scan of the aligned counts (every start is aligned, so
+//             start[e] = sum of align(count) over e' < e), psum, total,
 //             flags.
 //  3. scatter one wave per received row.  The stable rank of slot (r, k)
-//             among its expert's slots is the group's offset plus the number
-//             of that expert's slots in the earlier rows of the group plus
-//             those at k' < k in row r: two ballots over the group's ids.
-//             Destination = start[e] + rank; the row (16-byte chunks) and its
-//             scales are read once and written to each destination.  The
-//             same grid zero-fills the alignment pad rows and writes the row
-//             labels (grid-stride), so no extra pass is needed.
+//             among its expert's slots is its block's offset plus its
+//             group's offset in the block plus the number of that expert's
+//             slots in the earlier rows of the group plus those at k' < k in
+//             row r: two ballots over the group's ids.  Destination =
+//             start[e] + rank; the row (16-byte chunks) and its scales are
+//             read once and written to each destination.  The same grid
+//             zero-fills the alignment pad rows and writes the row labels
+//             (grid-stride), so no extra pass is needed.
 #include "common.hpp"
 
 namespace moe {
 namespace {
 
-constexpr int kGroupRows = 16;     // rows per counted group
-constexpr int kCountThreads = 256; // one row per thread: 16 groups per workgroup
-constexpr int kGroupsPerBlock = kCountThreads / kGroupRows;
+constexpr int kGroupRows = 16;      // rows per counted group
+constexpr int kCountThreads = 256;  // one row per thread: 16 groups per block
 constexpr int kScanThreads = 1024;
 constexpr int kScatterThreads = 256;
 constexpr int kRowsPerScatterBlock = kScatterThreads / 64;
 
+// Groups per count block (the [groups][E] count table stays in LDS).
+__host__ __device__ inline int groups_per_block(int) { return kCountThreads / kGroupRows; }
+constexpr int kFoldScanInts = 4096;  // block table size up to which the scatter scans it
+
 struct Workspace {
-  int32_t* grp;       // [ngroups][E]: counts, then exclusive offsets
-  int32_t* grp_flag;  // [ngroups]
+  int32_t* grp;       // [ngroups][E]: offset of each group within its block
+  int32_t* blk;       // [nblocks][E]: block totals, then exclusive block offsets
+  int32_t* blk_flag;  // [nblocks]
   int32_t* starts;    // [E]
   int32_t* padbase;   // [E + 1] exclusive prefix of pad rows per expert
 };
@@ -46,23 +55,29 @@ struct Workspace {
 __host__ __device__ inline int64_t num_groups(int64_t rows) {
   return (rows + kGroupRows - 1) / kGroupRows;
 }
+__host__ __device__ inline int64_t num_blocks(int64_t rows, int E) {
+  const int64_t br = (int64_t)groups_per_block(E) * kGroupRows;
+  return (rows + br - 1) / br;
+}
 
 __host__ __device__ inline size_t round256(size_t b) { return (b + 255) & ~size_t(255); }
 
 __host__ __device__ inline size_t workspace_bytes(int64_t rows, int E) {
-  int64_t ng = num_groups(rows);
-  return round256(size_t(ng) * E * 4) + round256(size_t(ng) * 4) + round256(size_t(E) * 4) +
-         round256(size_t(E + 1) * 4);
+  const int64_t ng = num_groups(rows), nb = num_blocks(rows, E);
+  return round256(size_t(ng) * E * 4) + round256(size_t(nb) * E * 4) + round256(size_t(nb) * 4) +
+         round256(size_t(E) * 4) + round256(size_t(E + 1) * 4);
 }
 
 __host__ __device__ inline Workspace carve(void* base, int64_t rows, int E) {
-  int64_t ng = num_groups(rows);
+  const int64_t ng = num_groups(rows), nb = num_blocks(rows, E);
   char* p = (char*)base;
   Workspace w;
   w.grp = (int32_t*)p;
   p += round256(size_t(ng) * E * 4);
-  w.grp_flag = (int32_t*)p;
-  p += round256(size_t(ng) * 4);
+  w.blk = (int32_t*)p;
+  p += round256(size_t(nb) * E * 4);
+  w.blk_flag = (int32_t*)p;
+  p += round256(size_t(nb) * 4);
   w.starts = (int32_t*)p;
   p += round256(size_t(E) * 4);
   w.padbase = (int32_t*)p;
@@ -71,33 +86,39 @@ __host__ __device__ inline Workspace carve(void* base, int64_t rows, int E) {
 
 __global__ __launch_bounds__(kCountThreads) void expand_count_kernel(
     const int32_t* __restrict__ ids, const int32_t* __restrict__ psum_rank, int nsrc,
-    int64_t rows, int topk, int E, int64_t ngroups, int32_t* __restrict__ grp,
-    int32_t* __restrict__ grp_flag) {
-  extern __shared__ int32_t cnt[];  // [kGroupsPerBlock][E], then flags
-  int32_t* lflag = cnt + kGroupsPerBlock * E;
+    int64_t rows, int topk, int E, int G, int64_t ngroups, int32_t* __restrict__ grp,
+    int32_t* __restrict__ blk, int32_t* __restrict__ blk_flag) {
+  extern __shared__ int32_t cnt[];  // [G][E]
+  __shared__ int lflag;
   const int t = threadIdx.x;
-  for (int i = t; i < kGroupsPerBlock * E; i += kCountThreads) cnt[i] = 0;
-  if (t < kGroupsPerBlock) lflag[t] = 0;
+  for (int i = t; i < G * E; i += kCountThreads) cnt[i] = 0;
+  if (t == 0) lflag = 0;
   __syncthreads();
   const int64_t nv = valid_rows(psum_rank, nsrc, rows);
-  const int64_t r = (int64_t)blockIdx.x * kCountThreads + t;
+  const int64_t r = (int64_t)blockIdx.x * G * kGroupRows + t;
   const int g = t / kGroupRows;
-  if (r < nv) {
+  if (t < G * kGroupRows && r < nv) {
     int bad = 0;
     for (int k = 0; k < topk; ++k) {
       const int e = ids[r * topk + k];
       if (e >= E) bad = 1;
       else if (e >= 0) atomicAdd(&cnt[g * E + e], 1);
     }
-    if (bad) atomicOr(&lflag[g], MOE_FLAG_EXPERT_ID_RANGE);
+    if (bad) atomicOr(&lflag, MOE_FLAG_EXPERT_ID_RANGE);
   }
   __syncthreads();
-  const int64_t g0 = (int64_t)blockIdx.x * kGroupsPerBlock;
-  for (int i = t; i < kGroupsPerBlock * E; i += kCountThreads) {
-    const int64_t gg = g0 + i / E;
-    if (gg < ngroups) grp[gg * E + i % E] = cnt[i];
+  // Per expert (one wave each, lane = group, G <= 64 lanes): each group's
+  // exclusive offset within the block (group order preserved), and the
+  // block total.
+  const int lane = t & 63, wid = t >> 6;
+  const int64_t g0 = (int64_t)blockIdx.x * G;
+  for (int e = wid; e < E; e += kCountThreads / 64) {
+    const int c = lane < G ? cnt[lane * E + e] : 0;
+    const int incl = wave_incl_scan_i(c);
+    if (lane < G && g0 + lane < ngroups) grp[(g0 + lane) * E + e] = incl - c;
+    if (lane == 63) blk[(int64_t)blockIdx.x * E + e] = incl;
   }
-  if (t < kGroupsPerBlock && g0 + t < ngroups) grp_flag[g0 + t] = lflag[t];
+  if (t == 0) blk_flag[blockIdx.x] = lflag;
 }
 
 // Exclusive scan over the whole 1024-thread workgroup; returns the exclusive
@@ -116,7 +137,7 @@ __device__ int block_excl_scan(int v, int* lds16, int* total) {
 }
 
 __global__ __launch_bounds__(kScanThreads) void expand_scan_kernel(
-    int32_t* __restrict__ grp, const int32_t* __restrict__ grp_flag, int64_t ngroups, int E,
+    int32_t* __restrict__ blk, const int32_t* __restrict__ blk_flag, int64_t nblocks, int E,
     int align, int64_t capacity, int32_t* __restrict__ starts, int32_t* __restrict__ padbase,
     int32_t* __restrict__ psum, int32_t* __restrict__ status) {
   __shared__ int lds_count[MOE_MAX_EXPERTS];
@@ -125,32 +146,32 @@ __global__ __launch_bounds__(kScanThreads) void expand_scan_kernel(
   const int t = threadIdx.x, lane = t & 63, wid = t >> 6;
   if (t == 0) lds_flag = 0;
   __syncthreads();
-  // Column scans: wave `wid` owns experts wid, wid+16, ...; lane l owns a
-  // contiguous run of groups so the order of groups is preserved.
-  const int64_t per = (ngroups + 63) / 64;
+  // Column scans over the block totals: wave `wid` owns experts wid, wid+16,
+  // ...; lane l owns a contiguous run of blocks so block order is preserved.
+  const int64_t per = (nblocks + 63) / 64;
   for (int e = wid; e < E; e += kScanThreads / 64) {
-    int64_t lo = lane * per, hi = min(lo + per, ngroups);
+    const int64_t lo = lane * per, hi = min(lo + per, nblocks);
     int s = 0;
-    for (int64_t g = lo; g < hi; ++g) s += grp[g * E + e];
-    int incl = wave_incl_scan_i(s);
+    for (int64_t b = lo; b < hi; ++b) s += blk[b * E + e];
+    const int incl = wave_incl_scan_i(s);
     int run = incl - s;
-    for (int64_t g = lo; g < hi; ++g) {
-      int c = grp[g * E + e];
-      grp[g * E + e] = run;
+    for (int64_t b = lo; b < hi; ++b) {
+      const int c = blk[b * E + e];
+      blk[b * E + e] = run;
       run += c;
     }
     if (lane == 63) lds_count[e] = incl;
   }
   int f = 0;
-  for (int64_t g = t; g < ngroups; g += kScanThreads) f |= grp_flag[g];
+  for (int64_t b = t; b < nblocks; b += kScanThreads) f |= blk_flag[b];
   if (f) atomicOr(&lds_flag, f);
   __syncthreads();
   const int cnt = t < E ? lds_count[t] : 0;
-  const int blk = align_up_i(cnt, align);
+  const int blk_rows = align_up_i(cnt, align);
   int total;
-  const int start = block_excl_scan(blk, lds16, &total);
+  const int start = block_excl_scan(blk_rows, lds16, &total);
   int padtot;
-  const int pb = block_excl_scan(blk - cnt, lds16, &padtot);
+  const int pb = block_excl_scan(blk_rows - cnt, lds16, &padtot);
   if (t < E) {
     starts[t] = start;
     psum[t] = start + cnt;
@@ -174,24 +195,101 @@ __device__ __forceinline__ int last_le(const int32_t* a, int n, int v) {
   return lo;
 }
 
+// Exclusive scan over a 256-thread workgroup of n <= 1024 values held as
+// v[i] (i < n); each thread owns a contiguous run of up to four.  Writes the
+// exclusive prefixes to out[i] and returns the total (all threads).
+__device__ int block_excl_scan_256(const int* v, int* out, int n, int* lds4) {
+  const int t = threadIdx.x, lane = t & 63, wid = t >> 6;
+  const int per = (n + kScatterThreads - 1) / kScatterThreads;
+  const int lo = min(n, t * per), hi = min(n, lo + per);
+  int sum = 0;
+  for (int i = lo; i < hi; ++i) sum += v[i];
+  const int incl = wave_incl_scan_i(sum);
+  if (lane == 63) lds4[wid] = incl;
+  __syncthreads();
+  int base = 0, total = 0;
+  for (int w = 0; w < kScatterThreads / 64; ++w) {
+    if (w < wid) base += lds4[w];
+    total += lds4[w];
+  }
+  int run = base + incl - sum;
+  for (int i = lo; i < hi; ++i) {
+    out[i] = run;
+    run += v[i];
+  }
+  __syncthreads();
+  return total;
+}
+
 __global__ __launch_bounds__(kScatterThreads) void expand_scatter_kernel(
     const uint8_t* __restrict__ x, int64_t x_stride, const uint8_t* __restrict__ x_scale,
     int64_t x_scale_stride_bytes, int scale_bytes, const int32_t* __restrict__ ids,
     const float* __restrict__ topk_w, const int32_t* __restrict__ psum_rank, int nsrc,
-    int64_t rows, int hidden, int topk, int E, int64_t capacity,
-    const int32_t* __restrict__ grp_off, const int32_t* __restrict__ starts_g,
-    const int32_t* __restrict__ padbase_g, const int32_t* __restrict__ psum_g,
-    const int32_t* __restrict__ status, uint8_t* __restrict__ ex, uint8_t* __restrict__ ex_scale,
+    int64_t rows, int hidden, int topk, int E, int64_t capacity, int align,
+    const int32_t* __restrict__ grp_off, const int32_t* __restrict__ blk_g, int G, int nblk,
+    const int32_t* __restrict__ blk_flag, int fold, const int32_t* __restrict__ starts_g,
+    const int32_t* __restrict__ padbase_g, int32_t* __restrict__ psum_g,
+    int32_t* __restrict__ status, uint8_t* __restrict__ ex, uint8_t* __restrict__ ex_scale,
     int32_t* __restrict__ m_indices, int32_t* __restrict__ src2dst, float* __restrict__ row_weight) {
   extern __shared__ int32_t lds[];
-  int32_t* l_starts = lds;            // [E]
-  int32_t* l_padbase = l_starts + E;  // [E + 1]
+  int32_t* l_starts = lds;                // [E]
+  int32_t* l_padbase = l_starts + E;      // [E + 1]
+  int32_t* l_psum = l_padbase + E + 1;    // [E]
+  int32_t* l_tmp = l_psum + E;            // [E]
+  int32_t* l_blk = l_tmp + E;             // [nblk][E] (fold)
+  __shared__ int lds4[4];
+  __shared__ int l_total, l_flag;
   const int t = threadIdx.x, lane = t & 63, wid = t >> 6;
-  for (int i = t; i < E; i += kScatterThreads) l_starts[i] = starts_g[i];
-  for (int i = t; i <= E; i += kScatterThreads) l_padbase[i] = padbase_g[i];
-  __syncthreads();
+  const int32_t* blk_off;  // exclusive per-block offsets, [nblk][E]
+  if (fold) {
+    // The scan over the (few) block totals, done by every workgroup: block
+    // offsets per expert, expert totals, aligned starts, pad prefix.
+    if (t == 0) l_flag = 0;
+    for (int e = t; e < E; e += kScatterThreads) {
+      int run = 0;
+      for (int b = 0; b < nblk; ++b) {
+        const int c = blk_g[(int64_t)b * E + e];
+        l_blk[b * E + e] = run;
+        run += c;
+      }
+      l_psum[e] = run;  // the count, for now
+    }
+    int f = 0;
+    for (int b = t; b < nblk; b += kScatterThreads) f |= blk_flag[b];
+    __syncthreads();
+    if (f) atomicOr(&l_flag, f);
+    for (int e = t; e < E; e += kScatterThreads) l_tmp[e] = align_up_i(l_psum[e], align);
+    __syncthreads();
+    const int total = block_excl_scan_256(l_tmp, l_starts, E, lds4);
+    for (int e = t; e < E; e += kScatterThreads) l_tmp[e] -= l_psum[e];  // pad rows
+    __syncthreads();
+    const int padtot = block_excl_scan_256(l_tmp, l_padbase, E, lds4);
+    for (int e = t; e < E; e += kScatterThreads) l_psum[e] += l_starts[e];
+    if (t == 0) {
+      l_padbase[E] = padtot;
+      l_total = total;
+    }
+    __syncthreads();
+    if (blockIdx.x == 0) {  // the layout's outputs
+      for (int e = t; e < E; e += kScatterThreads) psum_g[e] = l_psum[e];
+      if (t == 0) {
+        status[0] = total;
+        status[1] = l_flag | (total > capacity ? MOE_FLAG_CAPACITY_OVERFLOW : 0);
+      }
+    }
+    blk_off = l_blk;
+  } else {
+    for (int i = t; i < E; i += kScatterThreads) {
+      l_starts[i] = starts_g[i];
+      l_psum[i] = psum_g[i];
+    }
+    for (int i = t; i <= E; i += kScatterThreads) l_padbase[i] = padbase_g[i];
+    if (t == 0) l_total = status[0];
+    __syncthreads();
+    blk_off = blk_g;
+  }
   const int64_t nv = valid_rows(psum_rank, nsrc, rows);
-  const int total = status[0];
+  const int total = l_total;
   const int64_t nrows_ex = min((int64_t)total, capacity);
   const int nsc = hidden / kGroup;
   const int nch = hidden / 16;
@@ -220,7 +318,8 @@ __global__ __launch_bounds__(kScatterThreads) void expand_scatter_kernel(
       int rank = __popcll(__ballot(myid == e) & ((1ull << k) - 1ull));  // k' < k
 #pragma unroll
       for (int i = 0; i < 8; ++i) rank += __popcll(__ballot(prev[i] == e));
-      const int64_t dd = (int64_t)l_starts[e] + grp_off[g * E + e] + rank;
+      const int64_t dd =
+          (int64_t)l_starts[e] + blk_off[(g / G) * E + e] + grp_off[g * E + e] + rank;
       if (lane == k && dd < capacity) {
         d = (int)dd;
         if (row_weight) row_weight[d] = topk_w[r * topk + k];
@@ -283,7 +382,7 @@ __global__ __launch_bounds__(kScatterThreads) void expand_scatter_kernel(
   const int npad = l_padbase[E];
   for (int64_t p = wave0; p < npad; p += gwaves) {
     const int e = last_le(l_padbase, E, (int)p);
-    const int64_t row = (int64_t)psum_g[e] + (p - l_padbase[e]);
+    const int64_t row = (int64_t)l_psum[e] + (p - l_padbase[e]);
     if (row >= capacity) continue;
     u32x4* dst = reinterpret_cast<u32x4*>(ex + row * hidden);
     const u32x4 z = {0u, 0u, 0u, 0u};
@@ -341,30 +440,38 @@ extern "C" moe_status moe_expand_layout(
   Workspace w = carve(workspace, rows, E);
   const int scale_bytes = fmt == MOE_SCALE_F32 ? 4 : 1;
 
+  const int G = groups_per_block(E);
+  const int64_t nb = num_blocks(rows, E);
+  // Small block table: every scatter workgroup scans it itself (no scan
+  // kernel); otherwise the scan kernel does it once.
+  const bool fold = nb * E <= kFoldScanInts;
+  {
   if (ng > 0) {
-    const int64_t nblk = (rows + kCountThreads - 1) / kCountThreads;
-    const size_t lds = size_t(kGroupsPerBlock) * (E + 1) * 4;
-    hipLaunchKernelGGL(expand_count_kernel, dim3((unsigned)nblk), dim3(kCountThreads), lds, s,
-                       topk_ids, psum_recv_per_rank, num_src_ranks, rows, topk, E, ng, w.grp,
-                       w.grp_flag);
+    const size_t lds = size_t(G) * E * 4;
+    hipLaunchKernelGGL(expand_count_kernel, dim3((unsigned)nb), dim3(kCountThreads), lds, s,
+                       topk_ids, psum_recv_per_rank, num_src_ranks, rows, topk, E, G, ng, w.grp,
+                       w.blk, w.blk_flag);
     if (hipGetLastError() != hipSuccess) return MOE_ERR_LAUNCH;
   }
-  hipLaunchKernelGGL(expand_scan_kernel, dim3(1), dim3(kScanThreads), 0, s, w.grp, w.grp_flag, ng,
-                     E, align, capacity, w.starts, w.padbase, psum, status);
-  if (hipGetLastError() != hipSuccess) return MOE_ERR_LAUNCH;
-
+  if (!fold) {
+    hipLaunchKernelGGL(expand_scan_kernel, dim3(1), dim3(kScanThreads), 0, s, w.blk,
+                       w.blk_flag, nb, E, align, capacity, w.starts, w.padbase, psum, status);
+    if (hipGetLastError() != hipSuccess) return MOE_ERR_LAUNCH;
+  }
+  }
   // One wave per received row, and enough workgroups that the label fill and
   // the pad zeroing spread over the chip.
   int64_t grid = (rows + kRowsPerScatterBlock - 1) / kRowsPerScatterBlock;
   if (grid < 1024) grid = 1024;
   if (grid > 16384) grid = 16384;
-  const size_t lds = size_t(E) * 4 + size_t(E + 1) * 4;
+  const size_t lds = (size_t(4) * E + 1 + (fold ? size_t(nb) * E : 0)) * 4;
   hipLaunchKernelGGL(expand_scatter_kernel, dim3((unsigned)grid), dim3(kScatterThreads), lds, s,
                      (const uint8_t*)x, x_stride, (const uint8_t*)x_scale,
                      x_scale_stride * scale_bytes, scale_bytes, topk_ids, topk_weights,
-                     psum_recv_per_rank, num_src_ranks, rows, hidden, topk, E, capacity, w.grp,
-                     w.starts, w.padbase, psum, status, (uint8_t*)ex, (uint8_t*)ex_scale,
-                     m_indices, src2dst, row_weight);
+                     psum_recv_per_rank, num_src_ranks, rows, hidden, topk, E, capacity, align,
+                     w.grp, w.blk, G, (int)nb, w.blk_flag, fold ? 1 : 0, w.starts, w.padbase,
+                     psum, status, (uint8_t*)ex, (uint8_t*)ex_scale, m_indices, src2dst,
+                     row_weight);
   if (hipGetLastError() != hipSuccess) return MOE_ERR_LAUNCH;
   return MOE_OK;
 }
