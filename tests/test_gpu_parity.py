@@ -5,12 +5,19 @@ Bars:
   gather in fold mode and with weights: bit-exact;
 * grouped GEMM (bf16 out): the oracle rounds a float64 sum once; the GPU
   sums in fp32 inside the matrix cores and rounds once.  Bound per element:
-  one bf16 ulp of the oracle value plus 2^-16 * sum_k |a_k w_k| (a generous
-  allowance for the fp32 accumulation, far below bf16 resolution for
-  ordinary values but not for results that cancel to near zero);
-* activation quantisation: scales within 2 fp32 ulps (the GPU's expf may
-  differ from numpy's by an ulp), fp8 codes equal except rare neighbours at
-  rounding ties (< 0.1% of codes, never more than one step apart);
+  one bf16 ulp of the oracle value plus 2^-14 * sum_k |a_k w_k|: an allowance
+  for the matrix core's accumulation, far below bf16 resolution for ordinary
+  values but not for results that cancel to near zero.  The fp8 MFMA sums
+  its 128 products per K block with less care than sequential IEEE fp32
+  rounding: errors of up to 1.7 * 2^-16 * sum |a_k w_k| were measured on
+  strongly cancelling outputs (result ~ 2^-12 of the sum), so the bound is
+  four times that;
+* activation quantisation: scales within 4 fp32 ulps, fp8 codes equal
+  except rare neighbours at rounding ties (< 0.1% of codes, never more than
+  one step apart).  The scale bound: the GPU's expf and numpy's exp may each
+  be an ulp from exp(-g), so SiLU*up (one exp, an add, a divide, a multiply,
+  each rounded in fp32) can differ by ~2 ulps, the group amax with it, and
+  amax / 448 and the weight fold each round once more;
 * layer output (bf16): |gpu - oracle| <= 1e-2 + 2e-2 |oracle| elementwise
   (the stated bar), and, so that small outputs are not waved through by the
   absolute term, rms(gpu - oracle) <= 1% of rms(oracle) and max|gpu -
@@ -73,7 +80,7 @@ def abs_terms(a_q, a_s, w_q, w_s, m_indices, rows, fmt):
 
 def check_gemm(got, ref, terms, what):
     diff = np.abs(got.astype(np.float64) - ref)
-    bound = bf16_ulp(ref) + 2.0 ** -16 * terms
+    bound = bf16_ulp(ref) + 2.0 ** -14 * terms
     frac = (diff > 0).mean()
     worst = np.argsort((diff / bound).ravel())[-3:]
     print(f"{what}: {frac:.4f} of elements differ, max diff/bound "
@@ -115,6 +122,10 @@ SMALL = [
     ("tiny", dict(rows=40, valid_rows=23, src_ranks=4, tail_alias=True, seed=79)),
     ("tiny", dict(rows=200, hidden=512, inter=384, experts=5, global_experts=5, topk=2,
                   align=64, fmt="ue8m0", seed=82)),
+    # many experts: the layout's block table (15 blocks x 300 experts) is too
+    # large for the scatter to scan itself, so the separate scan kernel runs
+    ("tiny", dict(rows=3600, hidden=128, inter=128, experts=300, global_experts=600, topk=4,
+                  align=16, seed=83)),
 ]
 IDS = [f"{n}-{'-'.join(f'{k}{v}' for k, v in o.items())}" for n, o in SMALL]
 
@@ -222,7 +233,9 @@ def test_stages_against_oracle(name, over):
     mag = np.abs(fp8.decode_e4m3(L["dq"][live][diff]))
     assert np.all(step <= np.maximum(mag, 2.0 ** -6) * 2.0 ** -3 + 2.0 ** -9)
     if fmt == "f32":
-        assert np.allclose(ds[live], L["ds"][live], rtol=2.5e-7, atol=0)
+        ulps = np.abs(ds[live].view(np.int32).astype(np.int64)
+                      - L["ds"][live].view(np.int32).astype(np.int64))
+        assert ulps.max() <= 4, ulps.max()
     else:
         assert np.array_equal(ds[live], L["ds"][live])
     # GEMM2 on the oracle's dq/ds
