@@ -40,14 +40,29 @@ __global__ __launch_bounds__(kThreads) void act_quant_kernel(
     int inter, int E, const float* __restrict__ fold_w, uint8_t* __restrict__ out,
     uint8_t* __restrict__ out_scale) {
   const int t = threadIdx.x, lane = t & 63;
-  const int64_t nrows = min((int64_t)status[0], capacity);
   const int ngroups = inter / kGroup;
-  for (int64_t m = blockIdx.x; m < nrows; m += gridDim.x) {
-    const int e = m_indices[m];
+  // Round trip 1: the total and this workgroup's first label together (the
+  // grid never exceeds the capacity, so row blockIdx.x is in bounds).
+  int64_t m = blockIdx.x;
+  int e_next = m_indices[m];
+  const int64_t nrows = min((int64_t)status[0], capacity);
+  for (; m < nrows; m += gridDim.x) {
+    const int e = e_next;
+    if (m + gridDim.x < nrows) e_next = m_indices[m + gridDim.x];
     if (e < 0 || e >= E) continue;  // uniform per workgroup
+    // Round trip 2: the expert's end, the fold weight and the row's first
+    // pass, loaded together; a pad row's (unwritten) G values are never used.
+    const int pe = psum[e];
+    const float w = kFold ? fold_w[m] : 1.f;
+    const uint16_t* grow = gu + m * (int64_t)(2 * inter);
+    u32x4 gv0 = {0u, 0u, 0u, 0u}, uv0 = {0u, 0u, 0u, 0u};
+    if (t * 8 < inter) {
+      gv0 = *reinterpret_cast<const u32x4*>(grow + t * 8);
+      uv0 = *reinterpret_cast<const u32x4*>(grow + inter + t * 8);
+    }
     uint8_t* qrow = out + m * inter;
     // out_scale is K-block-major: scale (row m, group g) at g * capacity + m.
-    if (m >= psum[e]) {  // alignment pad row: zeros, G is not read
+    if (m >= pe) {  // alignment pad row: zeros
       for (int c = t; c < inter / 16; c += kThreads)
         reinterpret_cast<u32x4*>(qrow)[c] = u32x4{0u, 0u, 0u, 0u};
       for (int g = t; g < ngroups; g += kThreads) {
@@ -56,8 +71,6 @@ __global__ __launch_bounds__(kThreads) void act_quant_kernel(
       }
       continue;
     }
-    const float w = kFold ? fold_w[m] : 1.f;
-    const uint16_t* grow = gu + m * (int64_t)(2 * inter);
     // Each thread owns 8 consecutive columns per pass of kThreads*8 columns;
     // the 16 threads of a 128-column group are 16 consecutive lanes.
     for (int c0 = 0; c0 < inter; c0 += kThreads * 8) {
@@ -66,8 +79,8 @@ __global__ __launch_bounds__(kThreads) void act_quant_kernel(
       float y[8];
       float amax = 0.f;
       if (active) {
-        const u32x4 gv = *reinterpret_cast<const u32x4*>(grow + col);
-        const u32x4 uv = *reinterpret_cast<const u32x4*>(grow + inter + col);
+        const u32x4 gv = c0 == 0 ? gv0 : *reinterpret_cast<const u32x4*>(grow + col);
+        const u32x4 uv = c0 == 0 ? uv0 : *reinterpret_cast<const u32x4*>(grow + inter + col);
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           y[2 * i] = silu_mul(__uint_as_float(gv[i] << 16), __uint_as_float(uv[i] << 16));

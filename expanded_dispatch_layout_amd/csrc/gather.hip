@@ -44,15 +44,23 @@ __global__ __launch_bounds__(kThreads) void gather_kernel(
   __shared__ float l_w[MOE_MAX_TOPK];
   __shared__ int l_n;
   const int t = threadIdx.x, lane = t & 63;
-  const int64_t nv = valid_rows(psum_rank, nsrc, rows);
   const int nch = hidden / 8;  // 16-byte chunks of 8 bf16
   const bool weighted = topk_w != nullptr;
+  // The first row's slots are read together with the valid-row boundary
+  // (the grid never exceeds the row count, so row blockIdx.x is in bounds).
+  int d0 = -1;
+  float w0 = 1.f;
+  if (t < 64 && lane < topk) {
+    d0 = src2dst[(int64_t)blockIdx.x * topk + lane];
+    if (weighted) w0 = topk_w[(int64_t)blockIdx.x * topk + lane];
+  }
+  const int64_t nv = valid_rows(psum_rank, nsrc, rows);
   for (int64_t r = blockIdx.x; r < nv; r += gridDim.x) {
     // Live slots in k order, compacted into LDS by wave 0.
     if (t < 64) {
-      int d = -1;
-      float wk = 1.f;
-      if (lane < topk) {
+      int d = d0;
+      float wk = w0;
+      if (r != blockIdx.x && lane < topk) {
         d = src2dst[r * topk + lane];
         if (weighted) wk = topk_w[r * topk + lane];
       }

@@ -10,9 +10,9 @@
 //
 // Three kernels on one stream (two when the block table is small: every
 // scatter workgroup then scans it itself):
-//  1. count   one thread per received row; a block covers G 16-row groups
-//             (G = 64 when the per-group table fits LDS).  Order-free
-//             per-expert counts of every group (LDS atomics), then, per
+//  1. count   a block covers G = 16 16-row groups; its threads read the
+//             block's (row, k) ids coalesced, all loads in flight at once.
+//             Order-free per-expert counts of every group (LDS atomics), then, per
 //             expert, the exclusive offset of each group within the block
 //             and the block's total -> workspace.
 //  2. scan    one workgroup: per-expert exclusive scan over the block totals
@@ -91,21 +91,36 @@ __global__ __launch_bounds__(kCountThreads) void expand_count_kernel(
   extern __shared__ int32_t cnt[];  // [G][E]
   __shared__ int lflag;
   const int t = threadIdx.x;
+  // The block's ids, slot i * 256 + t of its (row, k) slots per thread: read
+  // coalesced, every load issued before any is used.
+  const int64_t r0 = (int64_t)blockIdx.x * G * kGroupRows;
+  const int nslots = (int)min((int64_t)G * kGroupRows, rows - r0) * topk;
+  const int32_t* bids = ids + r0 * topk;
+  int idv[MOE_MAX_TOPK];
+#pragma unroll
+  for (int i = 0; i < MOE_MAX_TOPK; ++i) {
+    const int sl = i * kCountThreads + t;
+    idv[i] = (i < topk && sl < nslots) ? bids[sl] : -1;
+  }
+  const int64_t nv = valid_rows(psum_rank, nsrc, rows);
   for (int i = t; i < G * E; i += kCountThreads) cnt[i] = 0;
   if (t == 0) lflag = 0;
   __syncthreads();
-  const int64_t nv = valid_rows(psum_rank, nsrc, rows);
-  const int64_t r = (int64_t)blockIdx.x * G * kGroupRows + t;
-  const int g = t / kGroupRows;
-  if (t < G * kGroupRows && r < nv) {
-    int bad = 0;
-    for (int k = 0; k < topk; ++k) {
-      const int e = ids[r * topk + k];
-      if (e >= E) bad = 1;
-      else if (e >= 0) atomicAdd(&cnt[g * E + e], 1);
+  // Rows of the block below the valid-row boundary.
+  const int nvb = (int)max((int64_t)0, min(nv - r0, (int64_t)G * kGroupRows));
+  int bad = 0;
+#pragma unroll
+  for (int i = 0; i < MOE_MAX_TOPK; ++i) {
+    if (i < topk) {
+      const int lr = (i * kCountThreads + t) / topk;  // row within the block
+      const int e = idv[i];
+      if (lr < nvb) {
+        if (e >= E) bad = 1;
+        else if (e >= 0) atomicAdd(&cnt[(lr / kGroupRows) * E + e], 1);
+      }
     }
-    if (bad) atomicOr(&lflag, MOE_FLAG_EXPERT_ID_RANGE);
   }
+  if (bad) atomicOr(&lflag, MOE_FLAG_EXPERT_ID_RANGE);
   __syncthreads();
   // Per expert (one wave each, lane = group, G <= 64 lanes): each group's
   // exclusive offset within the block (group order preserved), and the
@@ -221,6 +236,20 @@ __device__ int block_excl_scan_256(const int* v, int* out, int n, int* lds4) {
   return total;
 }
 
+// Ids of row r's group predecessors (up to 15 * topk <= 480 values, eight
+// per lane; -1 past them) and, in lane k < topk, of slot (r, k).
+__device__ __forceinline__ void load_row_ids(const int32_t* __restrict__ ids, int64_t r, int topk,
+                                             int lane, int* prev, int& myid) {
+  const int64_t g_first = r / kGroupRows * kGroupRows;
+  const int nprev = (int)(r - g_first) * topk;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const int idx = i * 64 + lane;
+    prev[i] = idx < nprev ? ids[g_first * topk + idx] : -1;
+  }
+  myid = lane < topk ? ids[r * topk + lane] : -1;
+}
+
 __global__ __launch_bounds__(kScatterThreads) void expand_scatter_kernel(
     const uint8_t* __restrict__ x, int64_t x_stride, const uint8_t* __restrict__ x_scale,
     int64_t x_scale_stride_bytes, int scale_bytes, const int32_t* __restrict__ ids,
@@ -240,24 +269,46 @@ __global__ __launch_bounds__(kScatterThreads) void expand_scatter_kernel(
   __shared__ int lds4[4];
   __shared__ int l_total, l_flag;
   const int t = threadIdx.x, lane = t & 63, wid = t >> 6;
+  const int64_t gwaves = (int64_t)gridDim.x * (kScatterThreads / 64);
+  const int64_t wave0 = (int64_t)blockIdx.x * (kScatterThreads / 64) + wid;
+  // The first row's ids do not depend on the scan below: load them first.
+  int prev[8], myid = -1;
+  if (wave0 < rows) load_row_ids(ids, wave0, topk, lane, prev, myid);
+  const int64_t nv = valid_rows(psum_rank, nsrc, rows);
   const int32_t* blk_off;  // exclusive per-block offsets, [nblk][E]
   if (fold) {
     // The scan over the (few) block totals, done by every workgroup: block
     // offsets per expert, expert totals, aligned starts, pad prefix.
-    if (t == 0) l_flag = 0;
-    for (int e = t; e < E; e += kScatterThreads) {
-      int run = 0;
-      for (int b = 0; b < nblk; ++b) {
-        const int c = blk_g[(int64_t)b * E + e];
-        l_blk[b * E + e] = run;
-        run += c;
-      }
-      l_psum[e] = run;  // the count, for now
-    }
+    for (int i = t; i < nblk * E; i += kScatterThreads) l_blk[i] = blk_g[i];
     int f = 0;
     for (int b = t; b < nblk; b += kScatterThreads) f |= blk_flag[b];
+    if (t == 0) l_flag = 0;
     __syncthreads();
     if (f) atomicOr(&l_flag, f);
+    if (nblk <= 8) {  // a thread per expert walks its few blocks
+      for (int e = t; e < E; e += kScatterThreads) {
+        int run = 0;
+        for (int b = 0; b < nblk; ++b) {
+          const int c = l_blk[b * E + e];
+          l_blk[b * E + e] = run;
+          run += c;
+        }
+        l_psum[e] = run;  // the count, for now
+      }
+    } else {  // a wave per expert scans 64 blocks at a time
+      for (int e = wid; e < E; e += kScatterThreads / 64) {
+        int carry = 0;
+        for (int b0 = 0; b0 < nblk; b0 += 64) {
+          const int b = b0 + lane;
+          const int c = b < nblk ? l_blk[b * E + e] : 0;
+          const int incl = wave_incl_scan_i(c);
+          if (b < nblk) l_blk[b * E + e] = carry + incl - c;
+          carry += __shfl(incl, 63, 64);
+        }
+        if (lane == 0) l_psum[e] = carry;
+      }
+    }
+    __syncthreads();
     for (int e = t; e < E; e += kScatterThreads) l_tmp[e] = align_up_i(l_psum[e], align);
     __syncthreads();
     const int total = block_excl_scan_256(l_tmp, l_starts, E, lds4);
@@ -288,57 +339,79 @@ __global__ __launch_bounds__(kScatterThreads) void expand_scatter_kernel(
     __syncthreads();
     blk_off = blk_g;
   }
-  const int64_t nv = valid_rows(psum_rank, nsrc, rows);
   const int total = l_total;
   const int64_t nrows_ex = min((int64_t)total, capacity);
   const int nsc = hidden / kGroup;
   const int nch = hidden / 16;
-  const int64_t gwaves = (int64_t)gridDim.x * (kScatterThreads / 64);
-  const int64_t wave0 = (int64_t)blockIdx.x * (kScatterThreads / 64) + wid;
 
   // ---- one wave per received row ----
   for (int64_t r = wave0; r < rows; r += gwaves) {
-    const int64_t g = r / kGroupRows;
-    const int64_t g_first = g * kGroupRows;
-    // Ids of the earlier rows of this group (up to 15 * topk <= 480 values,
-    // eight per lane), and of this row (lane k < topk holds slot k).
-    const int nprev = (int)(r - g_first) * topk;
-    int prev[8];
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const int idx = i * 64 + lane;
-      prev[i] = (idx < nprev && g_first + idx / topk < nv) ? ids[g_first * topk + idx] : -1;
+    if (r != wave0) load_row_ids(ids, r, topk, lane, prev, myid);
+    // Rows past the valid boundary route nowhere.  A valid row's group
+    // predecessors are valid too, so prev needs no such check.
+    if (r >= nv) myid = -1;
+    const bool mine = myid >= 0 && myid < E;
+    const uint64_t live = __ballot(mine);
+    if (live == 0) {
+      if (lane < topk) src2dst[r * topk + lane] = -1;
+      continue;
     }
-    const int myid = (lane < topk && r < nv) ? ids[r * topk + lane] : -1;
-    int d = -1;
-    const uint64_t live = __ballot(myid >= 0 && myid < E);
+    const int64_t g = r / kGroupRows;
+    // Loads that do not depend on the destinations, issued together: the
+    // row's first 8 KB, its first 64 scales, this slot's weight and the
+    // slot's block and group offsets.
+    const u32x4* src = reinterpret_cast<const u32x4*>(x + r * x_stride);
+    const uint8_t* srow = x_scale + r * x_scale_stride_bytes;
+    u32x4 v[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int c = u * 64 + lane;
+      if (c < nch) v[u] = src[c];
+    }
+    float sf = 0.f;
+    uint8_t sb = 0;
+    if (lane < nsc) {
+      if (scale_bytes == 4) sf = reinterpret_cast<const float*>(srow)[lane];
+      else sb = srow[lane];
+    }
+    float wt = 0.f;
+    int base = 0;
+    if (mine) {
+      if (row_weight) wt = topk_w[r * topk + lane];
+      base = l_starts[myid] + blk_off[(g / G) * E + myid] + grp_off[g * E + myid];
+    }
+    // Stable rank of each live slot among its expert's slots of the group:
+    // earlier rows' slots, then this row's slots at smaller k.
+    int rank = 0;
     for (uint64_t mm = live; mm; mm &= mm - 1) {
       const int k = __builtin_ctzll(mm);
       const int e = __shfl(myid, k, 64);
-      int rank = __popcll(__ballot(myid == e) & ((1ull << k) - 1ull));  // k' < k
+      int rk = __popcll(__ballot(myid == e) & ((1ull << k) - 1ull));
 #pragma unroll
-      for (int i = 0; i < 8; ++i) rank += __popcll(__ballot(prev[i] == e));
-      const int64_t dd =
-          (int64_t)l_starts[e] + blk_off[(g / G) * E + e] + grp_off[g * E + e] + rank;
-      if (lane == k && dd < capacity) {
+      for (int i = 0; i < 8; ++i) rk += __popcll(__ballot(prev[i] == e));
+      if (lane == k) rank = rk;
+    }
+    int d = -1;
+    if (mine) {
+      const int64_t dd = (int64_t)base + rank;
+      if (dd < capacity) {
         d = (int)dd;
-        if (row_weight) row_weight[d] = topk_w[r * topk + k];
+        if (row_weight) row_weight[d] = wt;
       }
     }
     if (lane < topk) src2dst[r * topk + lane] = d;
-    uint64_t mask = __ballot(d >= 0);
+    const uint64_t mask = __ballot(d >= 0);
     if (mask == 0) continue;
-    const u32x4* src = reinterpret_cast<const u32x4*>(x + r * x_stride);
     for (int c0 = 0; c0 < nch; c0 += 64 * 8) {
-      u32x4 v[8];
+      if (c0 > 0) {
 #pragma unroll
-      for (int u = 0; u < 8; ++u) {
-        const int c = c0 + u * 64 + lane;
-        if (c < nch) v[u] = src[c];
+        for (int u = 0; u < 8; ++u) {
+          const int c = c0 + u * 64 + lane;
+          if (c < nch) v[u] = src[c];
+        }
       }
       for (uint64_t mm = mask; mm; mm &= mm - 1) {
-        const int k = __builtin_ctzll(mm);
-        const int dk = __shfl(d, k, 64);
+        const int dk = __shfl(d, __builtin_ctzll(mm), 64);
         u32x4* dst = reinterpret_cast<u32x4*>(ex + (int64_t)dk * hidden);
 #pragma unroll
         for (int u = 0; u < 8; ++u) {
@@ -351,13 +424,9 @@ __global__ __launch_bounds__(kScatterThreads) void expand_scatter_kernel(
     // shuffle could read an inactive lane), the stores only where c < nsc.
     for (int c0 = 0; c0 < nsc; c0 += 64) {
       const int c = c0 + lane;
-      float sf = 0.f;
-      uint8_t sb = 0;
-      if (c < nsc) {
-        if (scale_bytes == 4)
-          sf = reinterpret_cast<const float*>(x_scale + r * x_scale_stride_bytes)[c];
-        else
-          sb = (x_scale + r * x_scale_stride_bytes)[c];
+      if (c0 > 0 && c < nsc) {
+        if (scale_bytes == 4) sf = reinterpret_cast<const float*>(srow)[c];
+        else sb = srow[c];
       }
       // ex_scale is K-block-major: scale (row dk, block c) at c * capacity + dk.
       for (uint64_t mm = mask; mm; mm &= mm - 1) {
