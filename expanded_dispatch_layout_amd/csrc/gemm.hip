@@ -24,7 +24,11 @@
 //    ahead by waves 0-3; activations and their scales (re-read by every N
 //    tile of the group, mostly L2 hits) in 2-4 slots sized to the group,
 //    loaded by waves 4-7.  vmcnt is per wave, so each stream keeps its own
-//    depth.  LDS -> registers runs one step ahead: while the matrix core
+//    depth.  Each wave's K loop is instantiated for its role (weights, or
+//    activations with na blocks per stage) and its live-tile count, so the
+//    per-stage load count and every vmcnt wait are compile-time: the loop
+//    issues about 175 instructions per step per wave, of which 12..16 are
+//    MFMAs and 48..64 the fp32 promotion.  LDS -> registers runs one step ahead: while the matrix core
 //    works on step k from registers, the wave reads step k+1's fragments.
 //    One bare s_barrier per step publishes the next stage and frees the
 //    slots of the step just moved into registers.
@@ -85,7 +89,9 @@ constexpr int SC_BASE = DATA_BYTES;
 constexpr int BSC_BYTES = 2048;              // an item's weight block scales, all K blocks
 constexpr int BSC_BASE = SC_BASE + kScSlots * SC_SLOT;
 constexpr int MAX_KB = BSC_BYTES / 4 - 1;    // K / 128 limit (fits BSC_BYTES incl. alignment)
-constexpr int LDS_BYTES = BSC_BASE + BSC_BYTES;  // 150 KB of the CU's 160 KB
+constexpr int DUMMY_BASE = BSC_BASE + BSC_BYTES;  // landing area of the padding loads
+constexpr int DUMMY_BYTES = 3 * 256;
+constexpr int LDS_BYTES = DUMMY_BASE + DUMMY_BYTES;  // 152 KB of the CU's 160 KB
 constexpr int kLoadWaves = 4;                // waves per stream: 0-3 weights, 4-7 activations
 constexpr int B_LOADS = B_BYTES / (kLoadWaves * 64 * 16);  // 16-byte loads per lane per stage
 constexpr int A_LOADS = A_BYTES / (kLoadWaves * 64 * 16);  // at most, for a full group
@@ -158,23 +164,24 @@ __device__ __forceinline__ void sched_fence() { __builtin_amdgcn_sched_barrier(0
 // All of this wave's LDS reads have returned.
 __device__ __forceinline__ void wait_lgkm0() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
 
-// Wait until at most n (0..2 * (A_LOADS + 1)) of this wave's vector-memory
-// operations are outstanding; s_waitcnt takes an immediate.
-__device__ __forceinline__ void wait_vmcnt_upto(int n) {
-  switch (n) {
-#define MOE_WAIT_CASE(k) \
-  case k:                \
-    wait_vmcnt<k>();     \
-    break;
-    MOE_WAIT_CASE(1) MOE_WAIT_CASE(2) MOE_WAIT_CASE(3) MOE_WAIT_CASE(4) MOE_WAIT_CASE(5)
-    MOE_WAIT_CASE(6) MOE_WAIT_CASE(7) MOE_WAIT_CASE(8) MOE_WAIT_CASE(9) MOE_WAIT_CASE(10)
-    MOE_WAIT_CASE(11) MOE_WAIT_CASE(12) MOE_WAIT_CASE(13) MOE_WAIT_CASE(14) MOE_WAIT_CASE(15)
-    MOE_WAIT_CASE(16) MOE_WAIT_CASE(17) MOE_WAIT_CASE(18)
-#undef MOE_WAIT_CASE
-    default: wait_vmcnt<0>(); break;  // 0, and anything unexpected: wait for all
+// Wait until at most a * NL of this wave's vector-memory operations are
+// outstanding, a in [0, MAXA] at run time (s_waitcnt takes an immediate: a
+// short compare chain picks it).
+template <int NL, int MAXA>
+__device__ __forceinline__ void wait_ahead(int a) {
+  if constexpr (MAXA <= 0) {
+    wait_vmcnt<0>();
+  } else {
+    if (a >= MAXA) wait_vmcnt<MAXA * NL>();
+    else wait_ahead<NL, MAXA - 1>(a);
   }
 }
-static_assert(kMaxASlots - 2 <= 2 && A_LOADS + 1 <= 9, "wait_vmcnt_upto covers 0..18");
+
+// Activation ring geometry for na 8-row blocks per loading wave per stage
+// (a slot holds 32 * na rows): slots that fit the ring.
+__host__ __device__ constexpr int act_slots(int na) { return na <= 4 ? 4 : (na == 5 ? 3 : 2); }
+static_assert(4 * 4 * 4096 <= A_RING && 3 * 5 * 4096 <= A_RING && 2 * 8 * 4096 <= A_RING,
+              "activation ring");
 
 struct Item {
   const uint8_t* a;     // first row of the group
@@ -188,8 +195,10 @@ struct Item {
   int KB;               // K / 128
   int K;
   int sbytes;           // 4 (fp32) or 1 (UE8M0)
-  int a_slot_bytes;     // activation slot: live rows rounded to 16, x 128 B
-  int na_slots;         // activation slots that fit (2..kMaxASlots)
+  int blocks;           // 8-row blocks holding live rows
+  int na;               // blocks per activation-loading wave per stage (1..8)
+  int a_slot_bytes;     // activation slot: 32 * na rows x 128 B
+  int na_slots;         // activation slots: act_slots(na)
 };
 
 // Byte offset of this lane's 16-byte chunk of row r in a [rows][K] operand:
@@ -210,52 +219,62 @@ __device__ __forceinline__ void load_item_wscales(const Item& it, uint32_t lds0,
 }
 
 // One wave's share of the direct-to-LDS loads of a K step, with the per-lane
-// source offsets computed once per item.  Load j of wave w covers the rows
-// (j * 4 + w) * 8 .. + 8 (8 lanes per 128-byte row), landing at the same
-// offset in the slot.
+// source offsets and the LDS offsets computed once per item.  Load j covers
+// one 8-row block (8 lanes per 128-byte row), landing at the block's offset
+// in the slot.
 //
-// Weights (waves 0-3): the N tile's 128 rows, B_LOADS loads per stage.
-// Activations (waves 4-7): the 8-row blocks that hold live rows (n of them;
-// rows past the live rows inside a loaded block reload the last live row),
-// and for the first of these waves the group's activation scales of the
-// step (one contiguous run: they are K-block-major; lane l brings rows
-// 4l..4l+3, lanes past the live rows re-read the last live row's word).
+// Weights (waves 0-3): wave w loads blocks j * 4 + w of the N tile's 128
+// rows, B_LOADS per stage.
+// Activations (waves 4-7): wave w loads blocks j * 4 + w that hold live
+// rows (rows past the live rows inside a block reload the last live row);
+// every loading wave issues exactly na loads per stage, the ones past its
+// share reloading the group's last block into its own place (same bytes, so
+// the duplicate write is harmless), so that the per-stage count is a
+// compile-time constant.  Then one scale load: the first of these waves
+// brings the group's activation scales of the step (one contiguous run:
+// K-block-major; lane l brings rows 4l..4l+3, lanes past the live rows
+// re-read the last live row's word), the others issue the same load into a
+// dummy area, again to keep the count fixed.
 struct WaveLoads {
   uint32_t off[A_LOADS];  // weights use the first B_LOADS
+  int lds_off[A_LOADS];
   uint32_t scale_off;
-  int n;                  // loads per stage (plus one for the scales)
-  bool scales;
+  uint32_t dummy;         // LDS address of this wave's dummy area
+  bool real_scales;
 
-  __device__ __forceinline__ void init(const Item& it, int wid, int lane) {
+  __device__ __forceinline__ void init(const Item& it, int wid, int lane, uint32_t lds0) {
     const bool wload = wid < kLoadWaves;
     const int w = wload ? wid : wid - kLoadWaves;
+    const int nreal = wload ? B_LOADS : max(0, min(it.na, (it.blocks - w + kLoadWaves - 1) / kLoadWaves));
 #pragma unroll
     for (int j = 0; j < A_LOADS; ++j) {
-      const int r = (j * kLoadWaves + w) * 8 + (lane >> 3);
+      const int b = j < nreal ? j * kLoadWaves + w : it.blocks - 1;
+      const int r = b * 8 + (lane >> 3);
       const int rr = wload ? r : min(r, it.live - 1);
       off[j] = row_chunk_offset(r, lane, it.K) - (uint32_t)(r - rr) * (uint32_t)it.K;
+      lds_off[j] = b * 1024;
     }
-    const int blocks = (it.live + 7) >> 3;
-    n = wload ? B_LOADS
-              : max(0, min(A_LOADS, (blocks - w + kLoadWaves - 1) / kLoadWaves));
-    scales = !wload && w == 0;
+    real_scales = !wload && w == 0;
+    dummy = lds0 + DUMMY_BASE + (uint32_t)(w > 0 ? w - 1 : 0) * 256u;
     const int l = (it.live - 1) >> 2;
     scale_off = (uint32_t)(lane < l ? lane : l) * (uint32_t)(4 * it.sbytes);
   }
   // Weights of one stage from src (row 0 at K block q) into the slot at lds.
-  __device__ __forceinline__ void weights(const uint8_t* src, uint32_t lds, int w) const {
+  __device__ __forceinline__ void weights(const uint8_t* src, uint32_t lds) const {
 #pragma unroll
-    for (int j = 0; j < B_LOADS; ++j) dma16(src, off[j], lds + (j * kLoadWaves + w) * 1024);
+    for (int j = 0; j < B_LOADS; ++j) dma16(src, off[j], lds + lds_off[j]);
   }
-  // Activations (and scales) of one stage.
-  __device__ __forceinline__ void acts(const uint8_t* src, uint32_t lds, int w,
-                                       const uint8_t* ssrc, uint32_t slds, bool f32) const {
+  // Activations (NA loads) and the scale load of one stage.
+  template <int NA>
+  __device__ __forceinline__ void acts(const uint8_t* src, uint32_t lds, const uint8_t* ssrc,
+                                       uint32_t slds, bool f32) const {
 #pragma unroll
-    for (int j = 0; j < A_LOADS; ++j)
-      if (j < n) dma16(src, off[j], lds + (j * kLoadWaves + w) * 1024);
-    if (scales) {
+    for (int j = 0; j < NA; ++j) dma16(src, off[j], lds + lds_off[j]);
+    if (real_scales) {
       if (f32) dma16(ssrc, scale_off, slds);
       else dma4(ssrc, scale_off, slds);
+    } else {
+      dma4(ssrc, scale_off, dummy);
     }
   }
 };
@@ -334,27 +353,34 @@ __device__ __forceinline__ void step(v8i (&a)[FM], v8i (&b)[FN], v4f (&acc)[FM][
     }
   } else {
     // fp32 scales: each 16x16 product is promoted into the accumulator
-    // (acc += P * sa * sb) while the matrix core runs the next product; two
-    // product registers in rotation.
+    // (acc += P * sa * sb) two MFMAs after it was issued, from three product
+    // registers in rotation.  The scheduling fences pin the order "MFMA t,
+    // then promote t-2": the result read was produced two matrix-core slots
+    // earlier, so the promotion needs no wait states and the matrix core
+    // always has the next product queued.
     const float sbv = lds_load<float>(bsc + kb * 4);
     v4f s4[NFM];
 #pragma unroll
     for (int i = 0; i < NFM; ++i)
       s4[i] = lds_load<v4f>(sc + (fo.s_row + i * ROW_TILE_STRIDE) * 4);
     sched_fence();
-    v4f p[2];
-    v4f scl;
+    constexpr int kLag = 2;
+    v4f p[kLag + 1];
+    v4f scl[NFM];
 #pragma unroll
-    for (int t = 0; t <= M; ++t) {
-      if (t < M) p[t & 1] = mfma_plain(a[t / FN], b[t % FN]);
-      if (t > 0) {
-        const int u = t - 1, i = u / FN, j = u % FN;
-        if (j == 0) {
+    for (int t = 0; t < M + kLag; ++t) {
+      if (t < M) p[t % (kLag + 1)] = mfma_plain(a[t / FN], b[t % FN]);
+      sched_fence();
+      if (t == 0) {
 #pragma unroll
-          for (int q = 0; q < 4; ++q) scl[q] = s4[i][q] * sbv;
-        }
+        for (int i = 0; i < NFM; ++i)
 #pragma unroll
-        for (int q = 0; q < 4; ++q) acc[i][j][q] += p[u & 1][q] * scl[q];
+          for (int q = 0; q < 4; ++q) scl[i][q] = s4[i][q] * sbv;
+      }
+      if (t >= kLag) {
+        const int u = t - kLag, i = u / FN, j = u % FN;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) acc[i][j][q] += p[u % (kLag + 1)][q] * scl[i][q];
       }
       if (t < M) refresh(t);
       sched_fence();
@@ -362,48 +388,37 @@ __device__ __forceinline__ void step(v8i (&a)[FM], v8i (&b)[FN], v4f (&acc)[FM][
   }
 }
 
-// The K loop of one item.  Each wave feeds one stream: weights (waves 0-3,
-// kBSlots - 1 stages ahead) or activations + scales (waves 4-7, na_slots - 1
-// stages ahead).  Step kb: wait for this wave's loads of stage kb+1 and for its
-// reads of step kb's fragments; barrier (stage kb+1 is now visible to every
-// wave, and every wave holds step kb's fragments in registers, so the slots
-// of stage kb are free); refill them with the next stage of the stream;
-// compute step kb from registers while reading step kb+1's fragments.
-template <bool kUe8m0, int NFM>
+// The K loop of one item for one wave.  ROLE 0: the wave streams weights
+// (kBSlots slots, kBSlots - 1 stages ahead); ROLE na > 0: it streams na
+// activation blocks + one scale load per stage (act_slots(na) slots).  Both
+// the per-stage load count and the depth are compile-time, so every vmcnt
+// wait is an immediate.  Step kb: wait for this wave's loads of stage kb+1
+// and for its reads of step kb's fragments; barrier (stage kb+1 is now
+// visible to every wave, and every wave holds step kb's fragments in
+// registers, so the slots of stage kb are free); refill them with the next
+// stage of the stream; compute step kb from registers while reading step
+// kb+1's fragments.
+template <bool kUe8m0, int NFM, int ROLE>
 __device__ __forceinline__ void kloop(uint32_t lds0, v4f (&acc)[FM][FN], const Item& it,
                                       const WaveLoads& wl, const FragOffsets& fo, int lane,
                                       int wid) {
+  constexpr bool kW = ROLE == 0;
+  constexpr int NL = kW ? W_LOADS : ROLE + 1;         // loads per stage
+  constexpr int D = kW ? kBSlots : act_slots(ROLE);   // stream depth (slots)
   const int KB = it.KB;
-  const bool wload = wid < kLoadWaves;
-  const int w = wload ? wid : wid - kLoadWaves;
-  const int D = wload ? kBSlots : it.na_slots;   // stream depth (slots)
-  const int nl = wl.n + (wl.scales ? 1 : 0);     // activation loads per stage
   const uint32_t a_end = lds0 + A_BASE + (uint32_t)(it.na_slots * it.a_slot_bytes);
-  // Wait for this wave's stage (issued - 1 - ahead): at most `ahead` later
-  // stages of its stream stay in flight.
-  auto wait_stage = [&](int ahead) {
-    if (wload) {
-      static_assert(kBSlots == 5, "weight-stream waits assume five slots");
-      if (ahead >= 3) wait_vmcnt<3 * W_LOADS>();
-      else if (ahead == 2) wait_vmcnt<2 * W_LOADS>();
-      else if (ahead == 1) wait_vmcnt<W_LOADS>();
-      else wait_vmcnt<0>();
-    } else {
-      wait_vmcnt_upto(ahead * nl);
-    }
-  };
   // Stream state: source pointers and destination slots of the next stage to
   // load, advanced one stage per issue.
-  const uint8_t* src = wload ? it.b : it.a;
-  const uint8_t* ssrc = it.as;
-  uint32_t bdst = lds0, adst = lds0 + A_BASE, sdst = lds0 + SC_BASE;
+  const uint8_t* src = uniform_ptr(kW ? it.b : it.a);
+  const uint8_t* ssrc = uniform_ptr(it.as);
+  uint32_t dst = kW ? lds0 : lds0 + A_BASE, sdst = lds0 + SC_BASE;
   auto issue = [&]() {
-    if (wload) {
-      wl.weights(src, bdst, w);
-      bdst = bdst + B_BYTES == lds0 + B_RING ? lds0 : bdst + B_BYTES;
+    if constexpr (kW) {
+      wl.weights(src, dst);
+      dst = dst + B_BYTES == lds0 + B_RING ? lds0 : dst + B_BYTES;
     } else {
-      wl.acts(src, adst, w, ssrc, sdst, !kUe8m0);
-      adst = adst + it.a_slot_bytes == a_end ? lds0 + A_BASE : adst + it.a_slot_bytes;
+      wl.template acts<ROLE>(src, dst, ssrc, sdst, !kUe8m0);
+      dst = dst + it.a_slot_bytes == a_end ? lds0 + A_BASE : dst + it.a_slot_bytes;
       sdst = sdst + SC_SLOT == lds0 + SC_BASE + kScSlots * SC_SLOT ? lds0 + SC_BASE
                                                                     : sdst + SC_SLOT;
       ssrc += it.as_kstride;
@@ -422,7 +437,7 @@ __device__ __forceinline__ void kloop(uint32_t lds0, v4f (&acc)[FM][FN], const I
   // stream's next stage into the last free slot.
   const int pre = min(D - 1, KB);
   for (int q = 0; q < pre; ++q) issue();
-  wait_stage(pre - 1);
+  wait_ahead<NL, D - 2>(pre - 1);
   barrier();
   v8i a[FM], b[FN];
   if constexpr (NFM > 0) {
@@ -436,7 +451,7 @@ __device__ __forceinline__ void kloop(uint32_t lds0, v4f (&acc)[FM][FN], const I
   if (issued < KB) { issue(); ++issued; }
   for (int kb = 0; kb + 1 < KB; ++kb) {
     // Stage kb+1 must have landed; the later stages issued may stay in flight.
-    wait_stage(issued - (kb + 2));
+    wait_ahead<NL, D - 2>(issued - (kb + 2));
     wait_lgkm0();
     barrier();
     if (issued < KB) { issue(); ++issued; }  // into the slots stage kb had
@@ -450,6 +465,24 @@ __device__ __forceinline__ void kloop(uint32_t lds0, v4f (&acc)[FM][FN], const I
   // by the previous barrier (or the prologue's).
   if constexpr (NFM > 0)
     step<kUe8m0, NFM, false>(a, b, acc, 0u, 0u, rs, bsc, it, fo, KB - 1, lane);
+}
+
+// The K loop instantiation for this wave's live-tile count and role.
+template <bool kUe8m0, int NFM>
+__device__ __forceinline__ void kloop_role(int role, uint32_t lds0, v4f (&acc)[FM][FN],
+                                           const Item& it, const WaveLoads& wl,
+                                           const FragOffsets& fo, int lane, int wid) {
+  switch (role) {  // uniform per wave
+    case 0: kloop<kUe8m0, NFM, 0>(lds0, acc, it, wl, fo, lane, wid); break;
+    case 1: kloop<kUe8m0, NFM, 1>(lds0, acc, it, wl, fo, lane, wid); break;
+    case 2: kloop<kUe8m0, NFM, 2>(lds0, acc, it, wl, fo, lane, wid); break;
+    case 3: kloop<kUe8m0, NFM, 3>(lds0, acc, it, wl, fo, lane, wid); break;
+    case 4: kloop<kUe8m0, NFM, 4>(lds0, acc, it, wl, fo, lane, wid); break;
+    case 5: kloop<kUe8m0, NFM, 5>(lds0, acc, it, wl, fo, lane, wid); break;
+    case 6: kloop<kUe8m0, NFM, 6>(lds0, acc, it, wl, fo, lane, wid); break;
+    case 7: kloop<kUe8m0, NFM, 7>(lds0, acc, it, wl, fo, lane, wid); break;
+    default: kloop<kUe8m0, NFM, 8>(lds0, acc, it, wl, fo, lane, wid); break;
+  }
 }
 
 template <bool kUe8m0>
@@ -510,8 +543,10 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(
     it.K = K;
     it.KB = KB;
     it.sbytes = sbytes;
-    it.a_slot_bytes = (((int)live + 15) & ~15) * BK;
-    it.na_slots = min(kMaxASlots, A_RING / it.a_slot_bytes);  // >= 2
+    it.blocks = ((int)live + 7) >> 3;
+    it.na = (it.blocks + kLoadWaves - 1) / kLoadWaves;  // 1..8
+    it.a_slot_bytes = it.na * 4096;
+    it.na_slots = act_slots(it.na);
     it.a = a + m0 * K;
     it.b = w + ((int64_t)e * N + (int64_t)nt * BN) * K;
     it.as = a_scale + m0 * sbytes;
@@ -532,14 +567,15 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(
       for (int j = 0; j < FN; ++j) acc[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
 
     WaveLoads wl;
-    wl.init(it, wid, lane);
+    wl.init(it, wid, lane, lds0);
+    const int role = wid < kLoadWaves ? 0 : it.na;
     wait_vmcnt<0>();  // nothing older (previous item's stores) left in flight
-    switch (nfm) {  // uniform per wave; one K loop per live-tile count
-      case 4: kloop<kUe8m0, 4>(lds0, acc, it, wl, fo, lane, wid); break;
-      case 3: kloop<kUe8m0, 3>(lds0, acc, it, wl, fo, lane, wid); break;
-      case 2: kloop<kUe8m0, 2>(lds0, acc, it, wl, fo, lane, wid); break;
-      case 1: kloop<kUe8m0, 1>(lds0, acc, it, wl, fo, lane, wid); break;
-      default: kloop<kUe8m0, 0>(lds0, acc, it, wl, fo, lane, wid); break;
+    switch (nfm) {  // uniform per wave; one K loop per live-tile count and role
+      case 4: kloop_role<kUe8m0, 4>(role, lds0, acc, it, wl, fo, lane, wid); break;
+      case 3: kloop_role<kUe8m0, 3>(role, lds0, acc, it, wl, fo, lane, wid); break;
+      case 2: kloop_role<kUe8m0, 2>(role, lds0, acc, it, wl, fo, lane, wid); break;
+      case 1: kloop_role<kUe8m0, 1>(role, lds0, acc, it, wl, fo, lane, wid); break;
+      default: kloop_role<kUe8m0, 0>(role, lds0, acc, it, wl, fo, lane, wid); break;
     }
     wait_lgkm0();
     barrier();  // every wave is done reading the slots
