@@ -230,17 +230,20 @@ __device__ __forceinline__ void load_item_wscales(const Item& it, uint32_t lds0,
 // every loading wave issues exactly na loads per stage, the ones past its
 // share reloading the group's last block into its own place (same bytes, so
 // the duplicate write is harmless), so that the per-stage count is a
-// compile-time constant.  Then one scale load: the first of these waves
-// brings the group's activation scales of the step (one contiguous run:
-// K-block-major; lane l brings rows 4l..4l+3, lanes past the live rows
-// re-read the last live row's word), the others issue the same load into a
-// dummy area, again to keep the count fixed.
+// compile-time constant.  Then one 4-byte-per-lane scale load (the scales
+// are K-block-major, so a step's scales of the group are one contiguous
+// run): with fp32 scales wave w brings rows w * 64 + lane; with UE8M0 the
+// first of these waves brings all of them (lane l: rows 4l..4l+3) and the
+// others issue the same load into a dummy area, again to keep the count
+// fixed.  Lanes past the live rows re-read the last live row's word.  No
+// branch: a branch would let the compiler sink the step's first MFMAs below
+// the loads.
 struct WaveLoads {
   uint32_t off[A_LOADS];  // weights use the first B_LOADS
   int lds_off[A_LOADS];
-  uint32_t scale_off;
-  uint32_t dummy;         // LDS address of this wave's dummy area
-  bool real_scales;
+  uint32_t scale_off;     // source offset of this lane's scale word
+  uint32_t scale_rel;     // its LDS offset within the scale slot
+  uint32_t dummy;         // LDS address of this wave's dummy area (0: none)
 
   __device__ __forceinline__ void init(const Item& it, int wid, int lane, uint32_t lds0) {
     const bool wload = wid < kLoadWaves;
@@ -254,10 +257,16 @@ struct WaveLoads {
       off[j] = row_chunk_offset(r, lane, it.K) - (uint32_t)(r - rr) * (uint32_t)it.K;
       lds_off[j] = b * 1024;
     }
-    real_scales = !wload && w == 0;
-    dummy = lds0 + DUMMY_BASE + (uint32_t)(w > 0 ? w - 1 : 0) * 256u;
-    const int l = (it.live - 1) >> 2;
-    scale_off = (uint32_t)(lane < l ? lane : l) * (uint32_t)(4 * it.sbytes);
+    if (it.sbytes == 4) {  // fp32: wave w, rows w * 64 + lane
+      scale_off = (uint32_t)min(w * 64 + lane, it.live - 1) * 4u;
+      scale_rel = (uint32_t)w * 256u;
+      dummy = 0;
+    } else {               // UE8M0: one wave, lane l -> rows 4l .. 4l+3
+      const int l = (it.live - 1) >> 2;
+      scale_off = (uint32_t)min(lane, l) * 4u;
+      scale_rel = 0;
+      dummy = w > 0 ? lds0 + DUMMY_BASE + (uint32_t)(w - 1) * 256u : 0u;
+    }
   }
   // Weights of one stage from src (row 0 at K block q) into the slot at lds.
   __device__ __forceinline__ void weights(const uint8_t* src, uint32_t lds) const {
@@ -267,15 +276,10 @@ struct WaveLoads {
   // Activations (NA loads) and the scale load of one stage.
   template <int NA>
   __device__ __forceinline__ void acts(const uint8_t* src, uint32_t lds, const uint8_t* ssrc,
-                                       uint32_t slds, bool f32) const {
+                                       uint32_t slds) const {
 #pragma unroll
     for (int j = 0; j < NA; ++j) dma16(src, off[j], lds + lds_off[j]);
-    if (real_scales) {
-      if (f32) dma16(ssrc, scale_off, slds);
-      else dma4(ssrc, scale_off, slds);
-    } else {
-      dma4(ssrc, scale_off, dummy);
-    }
+    dma4(ssrc, scale_off, dummy ? dummy : slds + scale_rel);
   }
 };
 
@@ -310,45 +314,97 @@ __device__ __forceinline__ v4f mfma_plain(const v8i& a, const v8i& b) {
                                                           127, 0, 127);
 }
 
-// One K step from registers: a[0..NFM) x b[0..FN) of step kb; the step's
-// activation scales come from scale slot `sc` (read first, so that waiting
-// for them never waits for the reads issued after them) and its weight
-// block scale from `bsc` (the item's scales at K block kb).  With kNext, the
-// fragments of step kb+1 replace the old ones as soon as the MFMAs that read
-// them are issued: A row tile i after MFMA (i, FN-1), B column tile j after
-// MFMA (NFM-1, j), from slots next_a / next_b.  NFM: how many of the wave's
-// four 16-row tiles hold live rows.
-template <bool kUe8m0, int NFM, bool kNext>
+// Scales of a K step, read from LDS during the step before (raw words), then
+// turned into their register form once those reads have long returned: for
+// fp32 scales early in the step itself (the first promotion comes two MFMAs
+// in), for UE8M0 at the end of the step before (the MFMAs take them as
+// operands).
+template <bool kUe8m0, int NFM>
+struct StepScales;
+template <int NFM>
+struct StepScales<false, NFM> {
+  v4f raw[NFM];   // activation scales of this lane's 4 rows per row tile
+  float wraw;     // the weight block scale
+  v4f scl[NFM];   // their products
+  __device__ __forceinline__ void read(uint32_t sc, uint32_t bsc, const Item&,
+                                       const FragOffsets& fo, int kb, int) {
+    wraw = lds_load<float>(bsc + kb * 4);
+#pragma unroll
+    for (int i = 0; i < NFM; ++i) raw[i] = lds_load<v4f>(sc + (fo.s_row + i * ROW_TILE_STRIDE) * 4);
+  }
+  __device__ __forceinline__ void finish(const Item&, const FragOffsets&, int, int) {
+#pragma unroll
+    for (int i = 0; i < NFM; ++i)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) scl[i][q] = raw[i][q] * wraw;
+  }
+};
+template <int NFM>
+struct StepScales<true, NFM> {
+  uint32_t raw[NFM];  // row r's exponent byte is byte r of the slot
+  uint32_t wraw;
+  int abyte[NFM];
+  int sbyte;
+  __device__ __forceinline__ void read(uint32_t sc, uint32_t bsc, const Item& it,
+                                       const FragOffsets& fo, int kb, int lane) {
+    const int arow = fo.s_row - (lane >> 4) * 4 + (lane & 15);  // this lane's A row
+    wraw = lds_load<uint32_t>(bsc + ((it.bs_skew + kb) & ~3));
+#pragma unroll
+    for (int i = 0; i < NFM; ++i)
+      raw[i] = lds_load<uint32_t>(sc + ((arow + i * ROW_TILE_STRIDE) & ~3));
+  }
+  __device__ __forceinline__ void finish(const Item& it, const FragOffsets& fo, int kb,
+                                         int lane) {
+    const int arow = fo.s_row - (lane >> 4) * 4 + (lane & 15);
+    const int bpos = it.bs_skew + kb;
+    sbyte = (int)((wraw >> (8 * (bpos & 3))) & 0xffu);
+#pragma unroll
+    for (int i = 0; i < NFM; ++i)
+      abyte[i] = (int)((raw[i] >> (8 * ((arow + i * ROW_TILE_STRIDE) & 3))) & 0xffu);
+  }
+};
+
+// One K step from registers: a[0..NFM) x b[0..FN) with the scales `cur`.
+// With kNext, the fragments of step kb+1 replace the old ones as soon as the
+// MFMAs that read them are issued (A row tile i after MFMA (i, FN-1), B
+// column tile j after MFMA (NFM-1, j), from slots next_a / next_b), step
+// kb+1's scales are read into `nxt` (slot next_sc), and `issue` (the wave's
+// loads for a later stage) runs in the shadow of the first MFMAs instead of
+// delaying them.  NFM: how many of the wave's four 16-row tiles hold live
+// rows.
+template <bool kUe8m0, int NFM, bool kNext, typename Issue>
 __device__ __forceinline__ void step(v8i (&a)[FM], v8i (&b)[FN], v4f (&acc)[FM][FN],
-                                     uint32_t next_a, uint32_t next_b, uint32_t sc, uint32_t bsc,
-                                     const Item& it, const FragOffsets& fo, int kb, int lane) {
+                                     StepScales<kUe8m0, NFM>& ss, uint32_t next_a,
+                                     uint32_t next_b, uint32_t next_sc, uint32_t bsc,
+                                     const Item& it, const FragOffsets& fo, int kb, int lane,
+                                     Issue&& issue) {
   constexpr int M = NFM * FN;  // MFMAs of this step
-  auto refresh = [&](int t) {  // after MFMA t
+  auto refresh = [&](int t) __attribute__((always_inline)) {  // after MFMA t
     if constexpr (kNext) {
       const int i = t / FN, j = t % FN;
       if (i == NFM - 1) b[j] = frag2(next_b + j * 2048, fo.b_lo, fo.b_hi);
       if (j == FN - 1) a[i] = frag2(next_a + i * A_TILE_STRIDE, fo.a_lo, fo.a_hi);
     }
   };
+  auto side = [&](int t) __attribute__((always_inline)) {  // after MFMA t: work not feeding this step
+    if (t == 0) {
+      if constexpr (!kUe8m0) ss.finish(it, fo, kb, lane);    // this step's products
+      if constexpr (kNext) ss.read(next_sc, bsc, it, fo, kb + 1, lane);
+    }
+    if constexpr (kUe8m0 && kNext)
+      if (t == M - 1) ss.finish(it, fo, kb + 1, lane);       // the next step's operands
+    if (t == (M > 1 ? 1 : 0)) issue();
+  };
   if constexpr (kUe8m0) {
-    const int arow = fo.s_row - (lane >> 4) * 4 + (lane & 15);  // this lane's A row
-    const int bpos = it.bs_skew + kb;
-    const uint32_t sbw = lds_load<uint32_t>(bsc + (bpos & ~3));
-    uint32_t aw[NFM];  // row r's exponent byte is byte r of the slot
+    // The exponent bytes are the MFMA's own scale operands.
 #pragma unroll
-    for (int i = 0; i < NFM; ++i)
-      aw[i] = lds_load<uint32_t>(sc + ((arow + i * ROW_TILE_STRIDE) & ~3));
-    sched_fence();
-    const int sbyte = (int)((sbw >> (8 * (bpos & 3))) & 0xffu);
-#pragma unroll
-    for (int i = 0; i < NFM; ++i) {
-      const int abyte = (int)((aw[i] >> (8 * ((arow + i * ROW_TILE_STRIDE) & 3))) & 0xffu);
-#pragma unroll
-      for (int j = 0; j < FN; ++j) {
-        acc[i][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a[i], b[j], acc[i][j], 0, 0,
-                                                                     0, abyte, 0, sbyte);
-        refresh(i * FN + j);
-      }
+    for (int t = 0; t < M; ++t) {
+      const int i = t / FN, j = t % FN;
+      acc[i][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a[i], b[j], acc[i][j], 0, 0, 0,
+                                                                   ss.abyte[i], 0, ss.sbyte);
+      sched_fence();
+      side(t);
+      refresh(t);
       sched_fence();
     }
   } else {
@@ -358,31 +414,21 @@ __device__ __forceinline__ void step(v8i (&a)[FM], v8i (&b)[FN], v4f (&acc)[FM][
     // then promote t-2": the result read was produced two matrix-core slots
     // earlier, so the promotion needs no wait states and the matrix core
     // always has the next product queued.
-    const float sbv = lds_load<float>(bsc + kb * 4);
-    v4f s4[NFM];
-#pragma unroll
-    for (int i = 0; i < NFM; ++i)
-      s4[i] = lds_load<v4f>(sc + (fo.s_row + i * ROW_TILE_STRIDE) * 4);
-    sched_fence();
     constexpr int kLag = 2;
     v4f p[kLag + 1];
-    v4f scl[NFM];
 #pragma unroll
     for (int t = 0; t < M + kLag; ++t) {
       if (t < M) p[t % (kLag + 1)] = mfma_plain(a[t / FN], b[t % FN]);
       sched_fence();
-      if (t == 0) {
-#pragma unroll
-        for (int i = 0; i < NFM; ++i)
-#pragma unroll
-          for (int q = 0; q < 4; ++q) scl[i][q] = s4[i][q] * sbv;
-      }
       if (t >= kLag) {
         const int u = t - kLag, i = u / FN, j = u % FN;
 #pragma unroll
-        for (int q = 0; q < 4; ++q) acc[i][j][q] += p[u % (kLag + 1)][q] * scl[i][q];
+        for (int q = 0; q < 4; ++q) acc[i][j][q] += p[u % (kLag + 1)][q] * ss.scl[i][q];
       }
-      if (t < M) refresh(t);
+      if (t < M) {
+        side(t);
+        refresh(t);
+      }
       sched_fence();
     }
   }
@@ -412,12 +458,12 @@ __device__ __forceinline__ void kloop(uint32_t lds0, v4f (&acc)[FM][FN], const I
   const uint8_t* src = uniform_ptr(kW ? it.b : it.a);
   const uint8_t* ssrc = uniform_ptr(it.as);
   uint32_t dst = kW ? lds0 : lds0 + A_BASE, sdst = lds0 + SC_BASE;
-  auto issue = [&]() {
+  auto issue = [&]() __attribute__((always_inline)) {
     if constexpr (kW) {
       wl.weights(src, dst);
       dst = dst + B_BYTES == lds0 + B_RING ? lds0 : dst + B_BYTES;
     } else {
-      wl.template acts<ROLE>(src, dst, ssrc, sdst, !kUe8m0);
+      wl.template acts<ROLE>(src, dst, ssrc, sdst);
       dst = dst + it.a_slot_bytes == a_end ? lds0 + A_BASE : dst + it.a_slot_bytes;
       sdst = sdst + SC_SLOT == lds0 + SC_BASE + kScSlots * SC_SLOT ? lds0 + SC_BASE
                                                                     : sdst + SC_SLOT;
@@ -425,8 +471,8 @@ __device__ __forceinline__ void kloop(uint32_t lds0, v4f (&acc)[FM][FN], const I
     }
     src += BK;
   };
-  // Read-side slots of stage kb+1, and the scale slot of stage kb.
-  uint32_t rb = lds0 + B_BYTES, ra = lds0 + A_BASE + it.a_slot_bytes, rs = lds0 + SC_BASE;
+  // Read-side slots of stage kb+1.
+  uint32_t rb = lds0 + B_BYTES, ra = lds0 + A_BASE + it.a_slot_bytes;
   const uint32_t bsc = lds0 + BSC_BASE;
 
   // The item's weight block scales: issued before this wave's stage 0, so
@@ -440,31 +486,47 @@ __device__ __forceinline__ void kloop(uint32_t lds0, v4f (&acc)[FM][FN], const I
   wait_ahead<NL, D - 2>(pre - 1);
   barrier();
   v8i a[FM], b[FN];
+  StepScales<kUe8m0, NFM> ss;
   if constexpr (NFM > 0) {
 #pragma unroll
     for (int j = 0; j < FN; ++j) b[j] = frag2(lds0 + j * 2048, fo.b_lo, fo.b_hi);
 #pragma unroll
     for (int i = 0; i < NFM; ++i)
       a[i] = frag2(lds0 + A_BASE + i * A_TILE_STRIDE, fo.a_lo, fo.a_hi);
+    ss.read(lds0 + SC_BASE, bsc, it, fo, 0, lane);
+    if constexpr (kUe8m0) ss.finish(it, fo, 0, lane);
   }
-  int issued = pre;  // stages of this wave's stream issued so far
-  if (issued < KB) { issue(); ++issued; }
-  for (int kb = 0; kb + 1 < KB; ++kb) {
-    // Stage kb+1 must have landed; the later stages issued may stay in flight.
-    wait_ahead<NL, D - 2>(issued - (kb + 2));
+  if (pre < KB) issue();  // stages 0 .. min(D, KB) - 1 are now in flight
+  // Read-side slot of stage kb+1's scales.
+  uint32_t rsn = lds0 + SC_BASE + SC_SLOT;
+  // Step kb (not the last): stage kb+1 must have landed, with `ahead` later
+  // stages of this wave's stream still in flight; then the step, with the
+  // stream's next stage (if any) issued in its shadow.
+  auto body = [&](int kb, auto&& wait, auto&& issue_fn) __attribute__((always_inline)) {
+    wait();
     wait_lgkm0();
     barrier();
-    if (issued < KB) { issue(); ++issued; }  // into the slots stage kb had
-    if constexpr (NFM > 0)
-      step<kUe8m0, NFM, true>(a, b, acc, ra, rb, rs, bsc, it, fo, kb, lane);
+    if constexpr (NFM > 0) {
+      step<kUe8m0, NFM, true>(a, b, acc, ss, ra, rb, rsn, bsc, it, fo, kb, lane, issue_fn);
+    } else {
+      issue_fn();
+    }
     rb = rb + B_BYTES == lds0 + B_RING ? lds0 : rb + B_BYTES;
     ra = ra + it.a_slot_bytes == a_end ? lds0 + A_BASE : ra + it.a_slot_bytes;
-    rs = rs + SC_SLOT == lds0 + SC_BASE + kScSlots * SC_SLOT ? lds0 + SC_BASE : rs + SC_SLOT;
-  }
-  // Last step: nothing left to read ahead or load; its scales were published
-  // by the previous barrier (or the prologue's).
+    rsn = rsn + SC_SLOT == lds0 + SC_BASE + kScSlots * SC_SLOT ? lds0 + SC_BASE : rsn + SC_SLOT;
+  };
+  // Steady state (kb < KB - D): D - 2 stages stay in flight and every step
+  // issues one more (into the slots stage kb had), without a branch, so the
+  // loads really sit in the shadow of the first MFMAs.
+  int kb = 0;
+  for (; kb < KB - D; ++kb)
+    body(kb, [] { wait_vmcnt<(D - 2) * NL>(); }, issue);
+  // Tail: every stage is issued; fewer remain in flight each step.
+  for (; kb + 1 < KB; ++kb)
+    body(kb, [&] { wait_ahead<NL, D - 2>(KB - kb - 2); }, [] {});
+  // Last step: nothing left to read ahead or load.
   if constexpr (NFM > 0)
-    step<kUe8m0, NFM, false>(a, b, acc, 0u, 0u, rs, bsc, it, fo, KB - 1, lane);
+    step<kUe8m0, NFM, false>(a, b, acc, ss, 0u, 0u, 0u, bsc, it, fo, KB - 1, lane, [] {});
 }
 
 // The K loop instantiation for this wave's live-tile count and role.
