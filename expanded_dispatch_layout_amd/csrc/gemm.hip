@@ -287,7 +287,7 @@ struct WaveLoads {
 // this lane's A and B fragments for row/column tile 0; row tile i adds
 // i * A_TILE_STRIDE, column tile j adds j * 2048.
 struct FragOffsets {
-  int a_lo, a_hi, b_lo, b_hi, s_row;
+  int a_lo, a_hi, b_lo, b_hi, m_row;
 };
 
 __device__ __forceinline__ FragOffsets frag_offsets(int lane, int wm, int wn) {
@@ -298,7 +298,7 @@ __device__ __forceinline__ FragOffsets frag_offsets(int lane, int wm, int wn) {
   f.a_hi = swz(ra, fk + 1);
   f.b_lo = swz(rb, fk);  // within a weight slot
   f.b_hi = swz(rb, fk + 1);
-  f.s_row = wm * 16 + (lane >> 4) * 4;  // first output row of this lane (row tile 0)
+  f.m_row = wm * 16 + frow;  // this lane's output row in row tile 0
   return f;
 }
 
@@ -323,20 +323,18 @@ template <bool kUe8m0, int NFM>
 struct StepScales;
 template <int NFM>
 struct StepScales<false, NFM> {
-  v4f raw[NFM];   // activation scales of this lane's 4 rows per row tile
-  float wraw;     // the weight block scale
-  v4f scl[NFM];   // their products
+  float raw[NFM];  // activation scale of this lane's row, per row tile
+  float wraw;      // the weight block scale
+  float scl[NFM];  // their products
   __device__ __forceinline__ void read(uint32_t sc, uint32_t bsc, const Item&,
                                        const FragOffsets& fo, int kb, int) {
     wraw = lds_load<float>(bsc + kb * 4);
 #pragma unroll
-    for (int i = 0; i < NFM; ++i) raw[i] = lds_load<v4f>(sc + (fo.s_row + i * ROW_TILE_STRIDE) * 4);
+    for (int i = 0; i < NFM; ++i) raw[i] = lds_load<float>(sc + (fo.m_row + i * ROW_TILE_STRIDE) * 4);
   }
   __device__ __forceinline__ void finish(const Item&, const FragOffsets&, int, int) {
 #pragma unroll
-    for (int i = 0; i < NFM; ++i)
-#pragma unroll
-      for (int q = 0; q < 4; ++q) scl[i][q] = raw[i][q] * wraw;
+    for (int i = 0; i < NFM; ++i) scl[i] = raw[i] * wraw;
   }
 };
 template <int NFM>
@@ -347,7 +345,7 @@ struct StepScales<true, NFM> {
   int sbyte;
   __device__ __forceinline__ void read(uint32_t sc, uint32_t bsc, const Item& it,
                                        const FragOffsets& fo, int kb, int lane) {
-    const int arow = fo.s_row - (lane >> 4) * 4 + (lane & 15);  // this lane's A row
+    const int arow = fo.m_row;  // this lane's activation row
     wraw = lds_load<uint32_t>(bsc + ((it.bs_skew + kb) & ~3));
 #pragma unroll
     for (int i = 0; i < NFM; ++i)
@@ -355,7 +353,7 @@ struct StepScales<true, NFM> {
   }
   __device__ __forceinline__ void finish(const Item& it, const FragOffsets& fo, int kb,
                                          int lane) {
-    const int arow = fo.s_row - (lane >> 4) * 4 + (lane & 15);
+    const int arow = fo.m_row;
     const int bpos = it.bs_skew + kb;
     sbyte = (int)((wraw >> (8 * (bpos & 3))) & 0xffu);
 #pragma unroll
@@ -400,8 +398,8 @@ __device__ __forceinline__ void step(v8i (&a)[FM], v8i (&b)[FN], v4f (&acc)[FM][
 #pragma unroll
     for (int t = 0; t < M; ++t) {
       const int i = t / FN, j = t % FN;
-      acc[i][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a[i], b[j], acc[i][j], 0, 0, 0,
-                                                                   ss.abyte[i], 0, ss.sbyte);
+      acc[i][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(b[j], a[i], acc[i][j], 0, 0, 0,
+                                                                   ss.sbyte, 0, ss.abyte[i]);
       sched_fence();
       side(t);
       refresh(t);
@@ -418,12 +416,12 @@ __device__ __forceinline__ void step(v8i (&a)[FM], v8i (&b)[FN], v4f (&acc)[FM][
     v4f p[kLag + 1];
 #pragma unroll
     for (int t = 0; t < M + kLag; ++t) {
-      if (t < M) p[t % (kLag + 1)] = mfma_plain(a[t / FN], b[t % FN]);
+      if (t < M) p[t % (kLag + 1)] = mfma_plain(b[t % FN], a[t / FN]);
       sched_fence();
       if (t >= kLag) {
         const int u = t - kLag, i = u / FN, j = u % FN;
 #pragma unroll
-        for (int q = 0; q < 4; ++q) acc[i][j][q] += p[u % (kLag + 1)][q] * ss.scl[i][q];
+        for (int q = 0; q < 4; ++q) acc[i][j][q] += p[u % (kLag + 1)][q] * ss.scl[i];
       }
       if (t < M) {
         side(t);
@@ -631,7 +629,6 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(
     WaveLoads wl;
     wl.init(it, wid, lane, lds0);
     const int role = wid < kLoadWaves ? 0 : it.na;
-    wait_vmcnt<0>();  // nothing older (previous item's stores) left in flight
     switch (nfm) {  // uniform per wave; one K loop per live-tile count and role
       case 4: kloop_role<kUe8m0, 4>(role, lds0, acc, it, wl, fo, lane, wid); break;
       case 3: kloop_role<kUe8m0, 3>(role, lds0, acc, it, wl, fo, lane, wid); break;
@@ -642,26 +639,23 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(
     wait_lgkm0();
     barrier();  // every wave is done reading the slots
 
-    // Epilogue: bf16 tile through LDS, then 16-byte stores of the live rows.
-    uint16_t* ct = reinterpret_cast<uint16_t*>(lds);
+    // Epilogue: the products are computed transposed (weights as the first
+    // MFMA operand), so each lane holds 4 consecutive columns of one row per
+    // tile: one 8-byte store each, live rows only, straight from registers.
+    uint16_t* obase = out + m0 * N + (int64_t)nt * BN + wn * WTN + (lane >> 4) * 4;
 #pragma unroll
-    for (int i = 0; i < FM; ++i)
+    for (int i = 0; i < FM; ++i) {
+      const int r = fo.m_row + i * ROW_TILE_STRIDE;
+      if (r < it.live) {
 #pragma unroll
-      for (int j = 0; j < FN; ++j)
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const int r = wm * 16 + i * ROW_TILE_STRIDE + (lane >> 4) * 4 + q;
-          const int c = wn * WTN + j * 16 + (lane & 15);
-          ct[r * BN + c] = f32_to_bf16_rne(acc[i][j][q]);
+        for (int j = 0; j < FN; ++j) {
+          const uint2 o = make_uint2(
+              (uint32_t)f32_to_bf16_rne(acc[i][j][0]) | ((uint32_t)f32_to_bf16_rne(acc[i][j][1]) << 16),
+              (uint32_t)f32_to_bf16_rne(acc[i][j][2]) | ((uint32_t)f32_to_bf16_rne(acc[i][j][3]) << 16));
+          *reinterpret_cast<uint2*>(obase + (int64_t)r * N + j * 16) = o;
         }
-    __syncthreads();
-    uint16_t* obase = out + m0 * N + (int64_t)nt * BN;
-    for (int li = t; li < it.live * (BN / 8); li += kThreads) {
-      const int r = li / (BN / 8), c8 = li % (BN / 8);
-      *reinterpret_cast<u32x4*>(obase + (int64_t)r * N + c8 * 8) =
-          *reinterpret_cast<const u32x4*>(ct + r * BN + c8 * 8);
+      }
     }
-    __syncthreads();
   }
 }
 
