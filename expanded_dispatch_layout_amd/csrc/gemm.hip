@@ -309,6 +309,14 @@ __device__ __forceinline__ v8i frag2(uint32_t base, int lo_off, int hi_off) {
              (int)hi[3]};
 }
 
+// Two floats -> packed bf16 pair (low = x), round to nearest even: one
+// v_cvt_pk_bf16_f32 on gfx950.
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint32_t pk_bf16(float x, float y) {
+  typedef float f2 __attribute__((ext_vector_type(2)));
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f2{x, y}, bf16x2_t));
+}
+
 __device__ __forceinline__ v4f mfma_plain(const v8i& a, const v8i& b) {
   return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, v4f{0.f, 0.f, 0.f, 0.f}, 0, 0, 0,
                                                           127, 0, 127);
@@ -553,6 +561,7 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(
     int K, int E, int align, uint16_t* __restrict__ out) {
   __shared__ __attribute__((aligned(16))) uint8_t lds[LDS_BYTES];
   __shared__ int gp[MOE_MAX_EXPERTS + 1];  // prefix of row groups per expert
+  __shared__ int pe[MOE_MAX_EXPERTS];      // psum, kept for the item decode
   const int t = threadIdx.x, lane = t & 63;
   const int wid = __builtin_amdgcn_readfirstlane(t >> 6);  // uniform per wave
   const int wm = wid / WAVES_N, wn = wid % WAVES_N;
@@ -570,9 +579,11 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(
       const int e = e0 + lane;
       int ng = 0;
       if (e < E) {
+        const int p_e = psum[e];
         const int64_t st = e ? align_up_i(psum[e - 1], align) : 0;
-        const int64_t en = min((int64_t)align_up_i(psum[e], align), nrows);
+        const int64_t en = min((int64_t)align_up_i(p_e, align), nrows);
         ng = en > st ? (int)((en - st + GM - 1) / GM) : 0;
+        pe[e] = p_e;
       }
       const int incl = wave_incl_scan_i(ng);
       if (e < E) gp[e] = run + incl - ng;
@@ -594,9 +605,9 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(
       else hi = mid - 1;
     }
     const int e = lo;
-    const int64_t st = e ? align_up_i(psum[e - 1], align) : 0;
+    const int64_t st = e ? align_up_i(pe[e - 1], align) : 0;
     const int64_t m0 = st + (int64_t)(gi - gp[e]) * GM;
-    const int64_t live = min((int64_t)GM, min((int64_t)psum[e], nrows) - m0);
+    const int64_t live = min((int64_t)GM, min((int64_t)pe[e], nrows) - m0);
     if (live <= 0) continue;  // only alignment padding: nothing to compute
     Item it;
     it.live = (int)live;
@@ -649,9 +660,8 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(
       if (r < it.live) {
 #pragma unroll
         for (int j = 0; j < FN; ++j) {
-          const uint2 o = make_uint2(
-              (uint32_t)f32_to_bf16_rne(acc[i][j][0]) | ((uint32_t)f32_to_bf16_rne(acc[i][j][1]) << 16),
-              (uint32_t)f32_to_bf16_rne(acc[i][j][2]) | ((uint32_t)f32_to_bf16_rne(acc[i][j][3]) << 16));
+          const uint2 o = make_uint2(pk_bf16(acc[i][j][0], acc[i][j][1]),
+                                     pk_bf16(acc[i][j][2], acc[i][j][3]));
           *reinterpret_cast<uint2*>(obase + (int64_t)r * N + j * 16) = o;
         }
       }

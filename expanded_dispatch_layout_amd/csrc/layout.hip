@@ -250,6 +250,59 @@ __device__ __forceinline__ void load_row_ids(const int32_t* __restrict__ ids, in
   myid = lane < topk ? ids[r * topk + lane] : -1;
 }
 
+// One received row's wave-level state: its ids, which of its slots are
+// local, and (for a row with a local slot) the loads that do not depend on
+// the destinations: the row's first 8 KB, its first 64 scales, each local
+// slot's weight and its group's offset within its block.
+struct RowFetch {
+  int prev[8];
+  int myid;
+  bool mine;
+  uint64_t live;
+  u32x4 v[8];
+  float sf;
+  uint8_t sb;
+  float wt;
+  int grp;
+
+  __device__ __forceinline__ void ids_of(const int32_t* __restrict__ ids, int64_t r, int64_t nv,
+                                         int topk, int E, int lane) {
+    load_row_ids(ids, r, topk, lane, prev, myid);
+    // Rows past the valid boundary route nowhere.  A valid row's group
+    // predecessors are valid too, so prev needs no such check.
+    if (r >= nv) myid = -1;
+    mine = myid >= 0 && myid < E;
+    live = __ballot(mine);
+  }
+  __device__ __forceinline__ void data_of(const uint8_t* __restrict__ x, int64_t x_stride,
+                                          const uint8_t* __restrict__ x_scale,
+                                          int64_t x_scale_stride_bytes, int scale_bytes,
+                                          const float* __restrict__ topk_w,
+                                          const int32_t* __restrict__ grp_off, bool weights,
+                                          int64_t r, int hidden, int topk, int E, int lane) {
+    const int nch = hidden / 16, nsc = hidden / kGroup;
+    const u32x4* src = reinterpret_cast<const u32x4*>(x + r * x_stride);
+    const uint8_t* srow = x_scale + r * x_scale_stride_bytes;
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int c = u * 64 + lane;
+      if (c < nch) v[u] = src[c];
+    }
+    sf = 0.f;
+    sb = 0;
+    if (lane < nsc) {
+      if (scale_bytes == 4) sf = reinterpret_cast<const float*>(srow)[lane];
+      else sb = srow[lane];
+    }
+    wt = 0.f;
+    grp = 0;
+    if (mine) {
+      if (weights) wt = topk_w[r * topk + lane];
+      grp = grp_off[(r / kGroupRows) * E + myid];
+    }
+  }
+};
+
 __global__ __launch_bounds__(kScatterThreads) void expand_scatter_kernel(
     const uint8_t* __restrict__ x, int64_t x_stride, const uint8_t* __restrict__ x_scale,
     int64_t x_scale_stride_bytes, int scale_bytes, const int32_t* __restrict__ ids,
@@ -271,10 +324,17 @@ __global__ __launch_bounds__(kScatterThreads) void expand_scatter_kernel(
   const int t = threadIdx.x, lane = t & 63, wid = t >> 6;
   const int64_t gwaves = (int64_t)gridDim.x * (kScatterThreads / 64);
   const int64_t wave0 = (int64_t)blockIdx.x * (kScatterThreads / 64) + wid;
-  // The first row's ids do not depend on the scan below: load them first.
-  int prev[8], myid = -1;
-  if (wave0 < rows) load_row_ids(ids, wave0, topk, lane, prev, myid);
+  // The first row's loads do not depend on the scan below: issue them
+  // first (ids, then the row's data if it has a local slot), so that the
+  // scan runs while they are in flight.
   const int64_t nv = valid_rows(psum_rank, nsrc, rows);
+  RowFetch f;
+  if (wave0 < rows) {
+    f.ids_of(ids, wave0, nv, topk, E, lane);
+    if (f.live)
+      f.data_of(x, x_stride, x_scale, x_scale_stride_bytes, scale_bytes, topk_w, grp_off,
+                row_weight != nullptr, wave0, hidden, topk, E, lane);
+  }
   const int32_t* blk_off;  // exclusive per-block offsets, [nblk][E]
   if (fold) {
     // The scan over the (few) block totals, done by every workgroup: block
@@ -346,68 +406,48 @@ __global__ __launch_bounds__(kScatterThreads) void expand_scatter_kernel(
 
   // ---- one wave per received row ----
   for (int64_t r = wave0; r < rows; r += gwaves) {
-    if (r != wave0) load_row_ids(ids, r, topk, lane, prev, myid);
-    // Rows past the valid boundary route nowhere.  A valid row's group
-    // predecessors are valid too, so prev needs no such check.
-    if (r >= nv) myid = -1;
-    const bool mine = myid >= 0 && myid < E;
-    const uint64_t live = __ballot(mine);
-    if (live == 0) {
+    if (r != wave0) {
+      f.ids_of(ids, r, nv, topk, E, lane);
+      if (f.live)
+        f.data_of(x, x_stride, x_scale, x_scale_stride_bytes, scale_bytes, topk_w, grp_off,
+                  row_weight != nullptr, r, hidden, topk, E, lane);
+    }
+    if (f.live == 0) {
       if (lane < topk) src2dst[r * topk + lane] = -1;
       continue;
     }
     const int64_t g = r / kGroupRows;
-    // Loads that do not depend on the destinations, issued together: the
-    // row's first 8 KB, its first 64 scales, this slot's weight and the
-    // slot's block and group offsets.
-    const u32x4* src = reinterpret_cast<const u32x4*>(x + r * x_stride);
-    const uint8_t* srow = x_scale + r * x_scale_stride_bytes;
-    u32x4 v[8];
-#pragma unroll
-    for (int u = 0; u < 8; ++u) {
-      const int c = u * 64 + lane;
-      if (c < nch) v[u] = src[c];
-    }
-    float sf = 0.f;
-    uint8_t sb = 0;
-    if (lane < nsc) {
-      if (scale_bytes == 4) sf = reinterpret_cast<const float*>(srow)[lane];
-      else sb = srow[lane];
-    }
-    float wt = 0.f;
-    int base = 0;
-    if (mine) {
-      if (row_weight) wt = topk_w[r * topk + lane];
-      base = l_starts[myid] + blk_off[(g / G) * E + myid] + grp_off[g * E + myid];
-    }
     // Stable rank of each live slot among its expert's slots of the group:
     // earlier rows' slots, then this row's slots at smaller k.
     int rank = 0;
-    for (uint64_t mm = live; mm; mm &= mm - 1) {
+    for (uint64_t mm = f.live; mm; mm &= mm - 1) {
       const int k = __builtin_ctzll(mm);
-      const int e = __shfl(myid, k, 64);
-      int rk = __popcll(__ballot(myid == e) & ((1ull << k) - 1ull));
+      const int e = __shfl(f.myid, k, 64);
+      int rk = __popcll(__ballot(f.myid == e) & ((1ull << k) - 1ull));
 #pragma unroll
-      for (int i = 0; i < 8; ++i) rk += __popcll(__ballot(prev[i] == e));
+      for (int i = 0; i < 8; ++i) rk += __popcll(__ballot(f.prev[i] == e));
       if (lane == k) rank = rk;
     }
     int d = -1;
-    if (mine) {
-      const int64_t dd = (int64_t)base + rank;
+    if (f.mine) {
+      const int64_t dd =
+          (int64_t)l_starts[f.myid] + blk_off[(g / G) * E + f.myid] + f.grp + rank;
       if (dd < capacity) {
         d = (int)dd;
-        if (row_weight) row_weight[d] = wt;
+        if (row_weight) row_weight[d] = f.wt;
       }
     }
     if (lane < topk) src2dst[r * topk + lane] = d;
     const uint64_t mask = __ballot(d >= 0);
     if (mask == 0) continue;
+    const u32x4* src = reinterpret_cast<const u32x4*>(x + r * x_stride);
+    const uint8_t* srow = x_scale + r * x_scale_stride_bytes;
     for (int c0 = 0; c0 < nch; c0 += 64 * 8) {
       if (c0 > 0) {
 #pragma unroll
         for (int u = 0; u < 8; ++u) {
           const int c = c0 + u * 64 + lane;
-          if (c < nch) v[u] = src[c];
+          if (c < nch) f.v[u] = src[c];
         }
       }
       for (uint64_t mm = mask; mm; mm &= mm - 1) {
@@ -416,7 +456,7 @@ __global__ __launch_bounds__(kScatterThreads) void expand_scatter_kernel(
 #pragma unroll
         for (int u = 0; u < 8; ++u) {
           const int c = c0 + u * 64 + lane;
-          if (c < nch) dst[c] = v[u];
+          if (c < nch) dst[c] = f.v[u];
         }
       }
     }
@@ -425,16 +465,16 @@ __global__ __launch_bounds__(kScatterThreads) void expand_scatter_kernel(
     for (int c0 = 0; c0 < nsc; c0 += 64) {
       const int c = c0 + lane;
       if (c0 > 0 && c < nsc) {
-        if (scale_bytes == 4) sf = reinterpret_cast<const float*>(srow)[c];
-        else sb = srow[c];
+        if (scale_bytes == 4) f.sf = reinterpret_cast<const float*>(srow)[c];
+        else f.sb = srow[c];
       }
       // ex_scale is K-block-major: scale (row dk, block c) at c * capacity + dk.
       for (uint64_t mm = mask; mm; mm &= mm - 1) {
         const int dk = __shfl(d, __builtin_ctzll(mm), 64);
         if (c < nsc) {
           const int64_t at = (int64_t)c * capacity + dk;
-          if (scale_bytes == 4) reinterpret_cast<float*>(ex_scale)[at] = sf;
-          else ex_scale[at] = sb;
+          if (scale_bytes == 4) reinterpret_cast<float*>(ex_scale)[at] = f.sf;
+          else ex_scale[at] = f.sb;
         }
       }
     }
