@@ -6,8 +6,8 @@
 // Modifications/Core (under UE8M0 scales the top-k weight is applied to the
 // down output rather than folded into the scale).
 //
-// One workgroup per token row; each thread owns up to four 16-byte chunks
-// (8 bf16 each) of the row.  The slots are summed in ascending k, each
+// Four token rows per workgroup; each thread owns up to four 16-byte chunks
+// (8 bf16 each) of a row.  The slots are summed in ascending k, each
 // product and sum rounded to fp32 (no contraction), with one bf16 rounding at
 // the end.  HBM-bound: reads A rows of expert output, writes R_v token rows
 // (non-temporal stores: the output is not re-read by this layer).
@@ -16,7 +16,7 @@
 namespace moe {
 namespace {
 
-constexpr int kThreads = 256;  // one token row per workgroup
+constexpr int kThreads = 256;  // four waves: one per row of a quad
 constexpr int kChunksPerThread = 4;  // 16-byte chunks; H <= 8192 in one pass
 
 __device__ __forceinline__ void acc8(float* a, const u32x4& v, float c, bool weighted) {
@@ -33,59 +33,76 @@ __device__ __forceinline__ void acc8(float* a, const u32x4& v, float c, bool wei
   }
 }
 
-// One workgroup per token row: every thread owns up to four 16-byte chunks
-// of the row, so all of a slot's loads are issued together and the row's
-// latency is one memory round trip per group of four slots.
+constexpr int kRowsPerBlock = 4;  // one wave reads each row's slot list
+
+// Zero-route rows, fp32 accumulation of row r's live slots (its n slots at
+// dsts / ws), bf16 rounding once, non-temporal 16-byte stores.
+__device__ __forceinline__ void store_row(uint16_t* __restrict__ out, int64_t r, int hidden,
+                                          const float (&a)[kChunksPerThread][8]) {
+  const int t = threadIdx.x, nch = hidden / 8;
+  u32x4* orow = reinterpret_cast<u32x4*>(out + r * hidden);
+#pragma unroll
+  for (int i = 0; i < kChunksPerThread; ++i) {
+    const int c = t + i * kThreads;
+    if (c < nch) {
+      u32x4 o;
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        o[j] = (uint32_t)f32_to_bf16_rne(a[i][2 * j]) |
+               ((uint32_t)f32_to_bf16_rne(a[i][2 * j + 1]) << 16);
+      __builtin_nontemporal_store(o, orow + c);
+    }
+  }
+}
+
+// Four token rows per workgroup (grid-stride over row quads).  Wave j reads
+// row j's slot list and compacts the live slots into LDS (one memory round
+// trip for the four rows); the rows without a live slot are stored (zeros)
+// first, so their stores are under way while the live rows' expert rows are
+// loaded: every thread owns up to four 16-byte chunks of the row, a slot's
+// loads are issued together, one round trip per group of four slots.  The
+// slots are summed in ascending k, each product and sum rounded to fp32 (no
+// contraction).
 __global__ __launch_bounds__(kThreads) void gather_kernel(
     const uint16_t* __restrict__ eo, const int32_t* __restrict__ src2dst,
     const float* __restrict__ topk_w, const int32_t* __restrict__ psum_rank, int nsrc,
     int64_t rows, int hidden, int topk, int64_t capacity, uint16_t* __restrict__ out) {
-  __shared__ int l_dst[MOE_MAX_TOPK];
-  __shared__ float l_w[MOE_MAX_TOPK];
-  __shared__ int l_n;
-  const int t = threadIdx.x, lane = t & 63;
+  __shared__ int l_dst[kRowsPerBlock][MOE_MAX_TOPK];
+  __shared__ float l_w[kRowsPerBlock][MOE_MAX_TOPK];
+  __shared__ int l_n[kRowsPerBlock];
+  const int t = threadIdx.x, lane = t & 63, wid = t >> 6;
   const int nch = hidden / 8;  // 16-byte chunks of 8 bf16
   const bool weighted = topk_w != nullptr;
-  // The first row's slots are read together with the valid-row boundary
-  // (the grid never exceeds the row count, so row blockIdx.x is in bounds).
-  int d0 = -1;
-  float w0 = 1.f;
-  if (t < 64 && lane < topk) {
-    d0 = src2dst[(int64_t)blockIdx.x * topk + lane];
-    if (weighted) w0 = topk_w[(int64_t)blockIdx.x * topk + lane];
-  }
   const int64_t nv = valid_rows(psum_rank, nsrc, rows);
-  for (int64_t r = blockIdx.x; r < nv; r += gridDim.x) {
-    // Live slots in k order, compacted into LDS by wave 0.
-    if (t < 64) {
-      int d = d0;
-      float wk = w0;
-      if (r != blockIdx.x && lane < topk) {
+  const int64_t nquads = (nv + kRowsPerBlock - 1) / kRowsPerBlock;
+  for (int64_t q = blockIdx.x; q < nquads; q += gridDim.x) {
+    const int64_t r0 = q * kRowsPerBlock;
+    if (wid < kRowsPerBlock) {  // wave j: row r0 + j's live slots, in k order
+      const int64_t r = r0 + wid;
+      int d = -1;
+      float wk = 1.f;
+      if (r < nv && lane < topk) {
         d = src2dst[r * topk + lane];
         if (weighted) wk = topk_w[r * topk + lane];
       }
-      const bool live = lane < topk && d >= 0 && d < capacity;
+      const bool live = r < nv && lane < topk && d >= 0 && d < capacity;
       const uint64_t mask = __ballot(live);
       if (live) {
         const int idx = __popcll(mask & ((1ull << lane) - 1ull));
-        l_dst[idx] = d;
-        l_w[idx] = wk;
+        l_dst[wid][idx] = d;
+        l_w[wid][idx] = wk;
       }
-      if (lane == 0) l_n = __popcll(mask);
+      if (lane == 0) l_n[wid] = r < nv ? __popcll(mask) : -1;
     }
     __syncthreads();
-    const int n = l_n;
-    float a[kChunksPerThread][8];
-#pragma unroll
-    for (int i = 0; i < kChunksPerThread; ++i)
-#pragma unroll
-      for (int j = 0; j < 8; ++j) a[i][j] = 0.f;
-    for (int k0 = 0; k0 < n; k0 += 4) {
-      u32x4 v[4][kChunksPerThread];
+    // Loads of one group of up to four slots of row j (starting at slot k0).
+    u32x4 v[4][kChunksPerThread];
+    auto load_slots = [&](int j, int k0, int n) {
 #pragma unroll
       for (int u = 0; u < 4; ++u) {
         if (k0 + u < n) {
-          const u32x4* src = reinterpret_cast<const u32x4*>(eo + (int64_t)l_dst[k0 + u] * hidden);
+          const u32x4* src =
+              reinterpret_cast<const u32x4*>(eo + (int64_t)l_dst[j][k0 + u] * hidden);
 #pragma unroll
           for (int i = 0; i < kChunksPerThread; ++i) {
             const int c = t + i * kThreads;
@@ -93,29 +110,43 @@ __global__ __launch_bounds__(kThreads) void gather_kernel(
           }
         }
       }
+    };
+    // The first live row's first slots are loaded before the zero rows are
+    // stored, so that those loads are not queued behind the stores.
+    int jl = -1;
+    for (int j = kRowsPerBlock - 1; j >= 0; --j)
+      if (l_n[j] > 0) jl = j;
+    if (jl >= 0) load_slots(jl, 0, l_n[jl]);
+    float a[kChunksPerThread][8];
+    // Rows without a live slot: zeros.
 #pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        if (k0 + u < n) {
-          const float wk = l_w[k0 + u];
+    for (int i = 0; i < kChunksPerThread; ++i)
 #pragma unroll
-          for (int i = 0; i < kChunksPerThread; ++i) acc8(a[i], v[u][i], wk, weighted);
+      for (int j = 0; j < 8; ++j) a[i][j] = 0.f;
+    for (int j = 0; j < kRowsPerBlock; ++j)
+      if (l_n[j] == 0) store_row(out, r0 + j, hidden, a);
+    // Rows with live slots.
+    for (int j = (jl >= 0 ? jl : kRowsPerBlock); j < kRowsPerBlock; ++j) {
+      const int n = l_n[j];
+      if (n <= 0) continue;
+#pragma unroll
+      for (int i = 0; i < kChunksPerThread; ++i)
+#pragma unroll
+        for (int jj = 0; jj < 8; ++jj) a[i][jj] = 0.f;
+      for (int k0 = 0; k0 < n; k0 += 4) {
+        if (j != jl || k0 > 0) load_slots(j, k0, n);
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          if (k0 + u < n) {
+            const float wk = l_w[j][k0 + u];
+#pragma unroll
+            for (int i = 0; i < kChunksPerThread; ++i) acc8(a[i], v[u][i], wk, weighted);
+          }
         }
       }
+      store_row(out, r0 + j, hidden, a);
     }
-    u32x4* orow = reinterpret_cast<u32x4*>(out + r * hidden);
-#pragma unroll
-    for (int i = 0; i < kChunksPerThread; ++i) {
-      const int c = t + i * kThreads;
-      if (c < nch) {
-        u32x4 o;
-#pragma unroll
-        for (int j = 0; j < 4; ++j)
-          o[j] = (uint32_t)f32_to_bf16_rne(a[i][2 * j]) |
-                 ((uint32_t)f32_to_bf16_rne(a[i][2 * j + 1]) << 16);
-        __builtin_nontemporal_store(o, orow + c);
-      }
-    }
-    __syncthreads();  // l_dst / l_n are rewritten for the next row
+    __syncthreads();  // the slot lists are rewritten for the next quad
   }
 }
 
@@ -138,7 +169,10 @@ extern "C" moe_status moe_gather(const void* expert_out, const int32_t* src2dst,
   if (hidden / 8 > kThreads * kChunksPerThread) return MOE_ERR_UNSUPPORTED;
   if (rows == 0) return MOE_OK;
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
-  const int64_t grid = rows < 4096 ? rows : 4096;  // grid-stride over the rows
+  // Grid-stride over row quads; 1024 workgroups keep every quad of the
+  // DeepSeek-V3-shape share resident at once.
+  const int64_t quads = (rows + kRowsPerBlock - 1) / kRowsPerBlock;
+  const int64_t grid = quads < 1024 ? quads : 1024;
   hipLaunchKernelGGL(gather_kernel, dim3((unsigned)grid), dim3(kThreads), 0, s,
                      (const uint16_t*)expert_out, src2dst, topk_weights, psum_recv_per_rank,
                      num_src_ranks, rows, hidden, topk, capacity, (uint16_t*)out);
