@@ -327,24 +327,31 @@ __global__ __launch_bounds__(kScatterThreads) void expand_scatter_kernel(
   // The first row's loads do not depend on the scan below: issue them
   // first (ids, then the row's data if it has a local slot), so that the
   // scan runs while they are in flight.
+  // The count kernel's block table (its first 256 entries, which is all of
+  // it for the DeepSeek-V3-shape share) is read before anything waits, so
+  // its round trip overlaps the ids'.
+  const int nbe = fold ? nblk * E : 0;
+  const int blk0 = t < nbe ? blk_g[t] : 0;
+  const int flg0 = (fold && t < nblk) ? blk_flag[t] : 0;
   const int64_t nv = valid_rows(psum_rank, nsrc, rows);
   RowFetch f;
-  if (wave0 < rows) {
-    f.ids_of(ids, wave0, nv, topk, E, lane);
-    if (f.live)
-      f.data_of(x, x_stride, x_scale, x_scale_stride_bytes, scale_bytes, topk_w, grp_off,
-                row_weight != nullptr, wave0, hidden, topk, E, lane);
-  }
+  if (wave0 < rows) f.ids_of(ids, wave0, nv, topk, E, lane);
+  // Stored now: its load was issued before the ids', so waiting for it here
+  // costs nothing, whereas after the row's loads the wait would cover them.
+  if (t < nbe) l_blk[t] = blk0;
+  if (wave0 < rows && f.live)
+    f.data_of(x, x_stride, x_scale, x_scale_stride_bytes, scale_bytes, topk_w, grp_off,
+              row_weight != nullptr, wave0, hidden, topk, E, lane);
   const int32_t* blk_off;  // exclusive per-block offsets, [nblk][E]
   if (fold) {
     // The scan over the (few) block totals, done by every workgroup: block
     // offsets per expert, expert totals, aligned starts, pad prefix.
-    for (int i = t; i < nblk * E; i += kScatterThreads) l_blk[i] = blk_g[i];
-    int f = 0;
-    for (int b = t; b < nblk; b += kScatterThreads) f |= blk_flag[b];
+    for (int i = t + kScatterThreads; i < nbe; i += kScatterThreads) l_blk[i] = blk_g[i];
+    int fl = flg0;
+    for (int b = t + kScatterThreads; b < nblk; b += kScatterThreads) fl |= blk_flag[b];
     if (t == 0) l_flag = 0;
     __syncthreads();
-    if (f) atomicOr(&l_flag, f);
+    if (fl) atomicOr(&l_flag, fl);
     if (nblk <= 8) {  // a thread per expert walks its few blocks
       for (int e = t; e < E; e += kScatterThreads) {
         int run = 0;
@@ -369,18 +376,37 @@ __global__ __launch_bounds__(kScatterThreads) void expand_scatter_kernel(
       }
     }
     __syncthreads();
-    for (int e = t; e < E; e += kScatterThreads) l_tmp[e] = align_up_i(l_psum[e], align);
-    __syncthreads();
-    const int total = block_excl_scan_256(l_tmp, l_starts, E, lds4);
-    for (int e = t; e < E; e += kScatterThreads) l_tmp[e] -= l_psum[e];  // pad rows
-    __syncthreads();
-    const int padtot = block_excl_scan_256(l_tmp, l_padbase, E, lds4);
-    for (int e = t; e < E; e += kScatterThreads) l_psum[e] += l_starts[e];
-    if (t == 0) {
-      l_padbase[E] = padtot;
-      l_total = total;
+    if (E <= 64) {  // one wave: aligned starts, pad prefix, psum, total
+      if (wid == 0) {
+        const int c = lane < E ? l_psum[lane] : 0;
+        const int al = align_up_i(c, align);
+        const int ia = wave_incl_scan_i(al);
+        const int ip = wave_incl_scan_i(al - c);
+        if (lane < E) {
+          l_starts[lane] = ia - al;
+          l_padbase[lane] = ip - (al - c);
+          l_psum[lane] = ia - al + c;
+        }
+        if (lane == 63) {
+          l_padbase[E] = ip;
+          l_total = ia;
+        }
+      }
+    } else {
+      for (int e = t; e < E; e += kScatterThreads) l_tmp[e] = align_up_i(l_psum[e], align);
+      __syncthreads();
+      const int total = block_excl_scan_256(l_tmp, l_starts, E, lds4);
+      for (int e = t; e < E; e += kScatterThreads) l_tmp[e] -= l_psum[e];  // pad rows
+      __syncthreads();
+      const int padtot = block_excl_scan_256(l_tmp, l_padbase, E, lds4);
+      for (int e = t; e < E; e += kScatterThreads) l_psum[e] += l_starts[e];
+      if (t == 0) {
+        l_padbase[E] = padtot;
+        l_total = total;
+      }
     }
     __syncthreads();
+    const int total = l_total;
     if (blockIdx.x == 0) {  // the layout's outputs
       for (int e = t; e < E; e += kScatterThreads) psum_g[e] = l_psum[e];
       if (t == 0) {
