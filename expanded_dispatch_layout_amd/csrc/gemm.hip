@@ -13,9 +13,12 @@
 //    weight slab is streamed from HBM exactly once.
 //  - Persistent grid, one workgroup per CU, walking the items of the
 //    device-side layout (read from psum, no host sync).  Items are numbered
-//    group-major, so the 32..56 N tiles of one row group are consecutive and
-//    land on one XCD (dispatch is round-robin over the 8 XCDs): that XCD keeps
-//    the group's activations in its L2 while it streams the expert's weights.
+//    expert by expert, N tile by N tile, with the expert's row groups
+//    innermost; consecutive items land on one XCD (dispatch is round-robin
+//    over the 8 XCDs, and the block -> item map undoes that), so the groups of
+//    an (expert, N tile) stream the same weights side by side and that XCD's
+//    L2 serves them, while neighbouring N tiles share the groups'
+//    activations.
 //  - K advances one 128-wide scale block per step = one
 //    v_mfma_scale_f32_16x16x128_f8f6f4 per 16x16 sub-tile.  Eight waves (two
 //    per SIMD) in a 4 x 2 grid, each owning 64 x 64 outputs (4 x 4 MFMA tiles).
@@ -597,14 +600,21 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(
   const int64_t slot = (int64_t)(blockIdx.x % kXcds) * per_xcd + blockIdx.x / kXcds;
 
   for (int64_t item = slot; item < nitems; item += gridDim.x) {
-    const int gi = (int)(item / NT), nt = (int)(item % NT);
-    int lo = 0, hi = E - 1;  // expert of group gi: last e with gp[e] <= gi
+    // Expert e's items are [NT * gp[e], NT * gp[e + 1]), N-tile-major with
+    // its row groups innermost: the groups of one (expert, N tile) share a
+    // weight stream and run side by side on one XCD, so its L2 serves the
+    // weights to all but one of them.
+    const int q = (int)(item / NT);
+    int lo = 0, hi = E - 1;  // last e with gp[e] <= q
     while (lo < hi) {
       const int mid = (lo + hi + 1) >> 1;
-      if (gp[mid] <= gi) lo = mid;
+      if (gp[mid] <= q) lo = mid;
       else hi = mid - 1;
     }
     const int e = lo;
+    const int ge = gp[e + 1] - gp[e];  // row groups of expert e (>= 1 here)
+    const int64_t local = item - (int64_t)NT * gp[e];
+    const int nt = (int)(local / ge), gi = gp[e] + (int)(local % ge);
     const int64_t st = e ? align_up_i(pe[e - 1], align) : 0;
     const int64_t m0 = st + (int64_t)(gi - gp[e]) * GM;
     const int64_t live = min((int64_t)GM, min((int64_t)pe[e], nrows) - m0);
