@@ -302,6 +302,32 @@ def main():
     roof["launch_gbs"] = {"gate_up": g1_bytes / gemm1_us / 1e3, "down": g2_bytes / gemm2_us / 1e3}
     roof["mfma_tflops"] = flops / t / 1e12
 
+    # Every stage against its own roofline: algorithmic bytes (and flops) per
+    # launch, over the stage's event window (which includes ~2 us of dispatch
+    # latency, so the small launch-bound stages read low here; the committed
+    # kernel-trace summaries give the kernels' own durations).
+    R, T, nv, E = wl.rows, wl.topk, inp["num_valid"], wl.experts
+    sH, sI = (H // 128) * sb, (I // 128) * sb
+    st_bytes = {
+        "expand_layout": nv * T * 8 + A * (H + sH) + m_used * (H + sH + 4) + R * T * 4
+                         + mod.capacity * 4,
+        "gemm_gate_up": g1_bytes,
+        "act_quant": A * 4 * I + m_used * (I + sI),
+        "gemm_down": g2_bytes,
+        "gather": A * 2 * H + nv * 2 * H + nv * T * 8,
+    }
+    st_flops = {"gemm_gate_up": g1_flops, "gemm_down": g2_flops}
+    stages = {}
+    for n in names:
+        us = stages_us[n]
+        rec = {"us": us, "bytes": st_bytes[n], "gbs": st_bytes[n] / us / 1e3}
+        rec["hbm_frac"] = rec["gbs"] / HBM_PEAK_GBS
+        if n in st_flops:
+            rec["flops"] = st_flops[n]
+            rec["tflops"] = st_flops[n] / us / 1e6
+            rec["mfma_frac"] = rec["tflops"] / FP8_PEAK_TFLOPS
+        stages[n] = rec
+
     cpu = None
     if not args.no_cpu_baseline:
         cpu = cpu_baseline(inp, wl, args.cpu_runs)
@@ -325,6 +351,7 @@ def main():
                    "align": wl.align, "scale_fmt": wl.fmt, "parallelism": "ep-rank share, 1 GPU",
                    "assignments": A, "expanded_rows": m_used, "capacity": mod.capacity},
         "stages_us": stages_us,
+        "stages": stages,
         "roofline": roof,
         "cpu_baseline": cpu,
     }
