@@ -17,7 +17,9 @@ It is a plain, slow, obviously-correct restatement of what the pages define:
              the row-to-expert labels.
 * ``layer``  block-scaled grouped GEMM, SiLU*up with per-group quantisation
              (and the top-k weight fold), the weighted gather, the whole
-             layer, and a per-token brute force that uses no layout at all.
+             layer, the standard (non-EP) path (bf16 rows quantised per
+             1x128 group, top-k weights and the routed scaling factor in the
+             gather), and a per-token brute force that uses no layout at all.
 
 Sources (cited by title and section in every function):
 

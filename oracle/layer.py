@@ -34,6 +34,19 @@ combined with their top-k weights.
   boundary are not produced (vLLM PR 54109, Design: results for inactive
   rows only need to be safe to discard).
 
+Standard (non-EP) path (SGLang moe_runner/deep_gemm.py source,
+``pre_permute_standard_to_deep_gemm`` and ``post_permute_deep_gemm_to_
+standard``): the tokens arrive as bf16 rows, every one local; each row is
+quantised per 1x128 group (``sglang_per_token_group_quant_fp8``, with UE8M0
+scales when the GEMM takes them) and scattered into the same compact
+128-aligned expert blocks; after the same GEMMs and activation the rows are
+reduced with the top-k weights and multiplied by the routed scaling factor
+(``post_reorder_deepgemm(..., routed_scaling_factor)``).  Readings: the
+input quantisation is the per-group rule of ``quant`` (the same rule as the
+activation quantisation); the top-k weight is applied in the gather in both
+scale formats, as that path does (no fold); the factor multiplies the fp32
+sum of the weighted rows, before the single bf16 rounding.
+
 Precision: the matmuls accumulate in float64 and round once to bf16; the
 activation and quantisation run in float32 (the precision the pages' kernels
 decide fp8 codes in); the gather accumulates in float32.
@@ -118,11 +131,12 @@ def act_quant(G, live, fmt: str, fold_weight=None):
     return q, s
 
 
-def gather(D, src2dst, num_valid: int, topk_weights=None):
-    """out[r] = bf16(sum_k c_k * D[src2dst[r, k]]) for r < num_valid, over
-    slots with src2dst >= 0 in ascending k, in float32 (c_k = 1 when
-    topk_weights is None, else topk_weights[r, k]).  Returns [num_valid, H]
-    float32 holding bf16 values."""
+def gather(D, src2dst, num_valid: int, topk_weights=None, scale: float = 1.0):
+    """out[r] = bf16(scale * sum_k c_k * D[src2dst[r, k]]) for r < num_valid,
+    over slots with src2dst >= 0 in ascending k, in float32 (c_k = 1 when
+    topk_weights is None, else topk_weights[r, k]; scale is the routed
+    scaling factor, 1 on the expand path).  Returns [num_valid, H] float32
+    holding bf16 values."""
     D = np.asarray(D, dtype=np.float32)
     src = np.asarray(src2dst)
     acc = np.zeros((num_valid, D.shape[1]), dtype=np.float32)
@@ -136,17 +150,20 @@ def gather(D, src2dst, num_valid: int, topk_weights=None):
             c = np.asarray(topk_weights, dtype=np.float32)[:num_valid, k][ok]
             term = (term * c[:, None]).astype(np.float32)
         acc[ok] = (acc[ok] + term).astype(np.float32)
+    acc = (acc * np.float32(scale)).astype(np.float32)
     return fp8.round_bf16(acc)
 
 
-def layer(inp, mode: str = "auto"):
+def layer(inp, mode: str = "auto", routed_scaling_factor: float = 1.0):
     """The whole path on one rank.  `inp` holds: x_q [R,H] u8, x_s, ids [R,T],
     w [R,T] f32, num_valid, w13_q [E,2I,H], w13_s, w2_q [E,H,I], w2_s,
     align, fmt ('f32' | 'ue8m0'), cap (optional).
 
     mode: 'fold' (weight folded into the down GEMM's input scales; fp32 only),
     'post' (weight applied in the gather), or 'auto' (fold for fp32 scales,
-    post for UE8M0, as the pages do).  Returns a dict of every stage."""
+    post for UE8M0, as the pages do).  routed_scaling_factor multiplies the
+    gathered sum (the standard path's factor; 1 on the expand path).
+    Returns a dict of every stage."""
     from .layout import expand, capacity
     fmt = inp["fmt"]
     if mode == "auto":
@@ -169,9 +186,41 @@ def layer(inp, mode: str = "auto"):
     D = grouped_gemm(dq, ds, inp["w2_q"], inp["w2_s"], lay["m_indices"], n,
                      fmt, live=live)
     out = gather(D, lay["src2dst"], nv,
-                 topk_weights=None if mode == "fold" else inp["w"])
+                 topk_weights=None if mode == "fold" else inp["w"],
+                 scale=routed_scaling_factor)
     lay.update(G=G, dq=dq, ds=ds, D=D, out=out, live=live, mode=mode, cap=cap)
     return lay
+
+
+def quantize_input(x_bf16, num_valid: int, fmt: str):
+    """Standard path input: bf16 rows [R, H] (uint16 bits) -> fp8 codes and
+    per-1x128 scales of the rows below num_valid (rows past it: zeros, never
+    read)."""
+    bits = np.asarray(x_bf16, dtype=np.uint16)
+    R, H = bits.shape
+    x_q = np.zeros((R, H), np.uint8)
+    x_s = np.zeros((R, H // quant.GROUP), np.float32 if fmt == "f32" else np.uint8)
+    if num_valid > 0:
+        x_q[:num_valid], x_s[:num_valid] = quant.quantize_rows(
+            fp8.bf16_from_bits(bits[:num_valid]), fmt)
+    return x_q, x_s
+
+
+def standard_layer(inp):
+    """The standard (non-EP) path: `inp` as for `layer` but with x_bf16
+    [R, H] (uint16 bf16 bits) in place of x_q / x_s, an optional
+    routed_scaling_factor (default 1) and num_valid (default R).  The rows
+    are quantised per 1x128 group, then the layer runs with the top-k weight
+    applied in the gather, times the routed scaling factor."""
+    R = np.asarray(inp["x_bf16"]).shape[0]
+    nv = int(inp.get("num_valid", R))
+    x_q, x_s = quantize_input(inp["x_bf16"], nv, inp["fmt"])
+    inner = {k: v for k, v in inp.items() if k != "x_bf16"}
+    inner.update(x_q=x_q, x_s=x_s, num_valid=nv)
+    res = layer(inner, mode="post",
+                routed_scaling_factor=float(inp.get("routed_scaling_factor", 1.0)))
+    res.update(x_q=x_q, x_s=x_s)
+    return res
 
 
 def brute_force(inp, mode: str = "auto", rows=None):
@@ -182,10 +231,17 @@ def brute_force(inp, mode: str = "auto", rows=None):
     the slots in ascending k in fp32 before one bf16 rounding.
 
     rows: optional list of valid row indices to evaluate (default: all);
-    the result has one output row per entry, in that order."""
+    the result has one output row per entry, in that order.
+
+    Standard-path inputs (x_bf16 instead of x_q / x_s): each row is
+    quantised per 1x128 group first, the weights are applied to the down
+    output, and the sum is multiplied by routed_scaling_factor (default 1)
+    before the rounding."""
     fmt = inp["fmt"]
+    std = "x_bf16" in inp
     if mode == "auto":
-        mode = "fold" if fmt == "f32" else "post"
+        mode = "post" if std or fmt != "f32" else "fold"
+    rscale = np.float32(inp.get("routed_scaling_factor", 1.0))
     ids = np.asarray(inp["ids"])
     wts = np.asarray(inp["w"], dtype=np.float32)
     w13_q, w13_s = np.asarray(inp["w13_q"]), np.asarray(inp["w13_s"])
@@ -197,20 +253,28 @@ def brute_force(inp, mode: str = "auto", rows=None):
     assert all(0 <= r < nv for r in rows)
     cache13, cache2 = {}, {}
 
+    def cached(cache, e, q, s):
+        if e not in cache:
+            if len(cache) >= 16:    # bounds host memory at full size
+                cache.clear()
+            cache[e] = quant.dequant_block(q[e], s[e], fmt)
+        return cache[e]
+
     def w13_of(e):
-        if e not in cache13:
-            cache13[e] = quant.dequant_block(w13_q[e], w13_s[e], fmt)
-        return cache13[e]
+        return cached(cache13, e, w13_q, w13_s)
 
     def w2_of(e):
-        if e not in cache2:
-            cache2[e] = quant.dequant_block(w2_q[e], w2_s[e], fmt)
-        return cache2[e]
+        return cached(cache2, e, w2_q, w2_s)
 
     out = np.zeros((len(rows), H), dtype=np.float32)
     for i, r in enumerate(rows):
-        xr = quant.dequant_rows(np.asarray(inp["x_q"])[r:r + 1],
-                                np.asarray(inp["x_s"])[r:r + 1], fmt)
+        if std:
+            xq, xs = quant.quantize_rows(
+                fp8.bf16_from_bits(np.asarray(inp["x_bf16"])[r:r + 1]), fmt)
+            xr = quant.dequant_rows(xq, xs, fmt)
+        else:
+            xr = quant.dequant_rows(np.asarray(inp["x_q"])[r:r + 1],
+                                    np.asarray(inp["x_s"])[r:r + 1], fmt)
         acc = np.zeros(H, dtype=np.float32)
         for k in range(ids.shape[1]):
             e = int(ids[r, k])
@@ -226,5 +290,5 @@ def brute_force(inp, mode: str = "auto", rows=None):
             if mode == "post":
                 d = (d * wts[r, k]).astype(np.float32)
             acc = (acc + d).astype(np.float32)
-        out[i] = fp8.round_bf16(acc)
+        out[i] = fp8.round_bf16((acc * rscale).astype(np.float32))
     return out

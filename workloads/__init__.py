@@ -22,6 +22,14 @@ padded             8192-row receive buffer, 1536 valid rows (boundary
                    random-byte tail with ids -1; rest as dsv3
 padded_alias       as padded but the tail's ids alias valid local ids
 dsv3_local         as dsv3 but every row has at least one local slot
+std_tiny           standard (non-EP) path: bf16 input rows, 64 rows,
+                   H=256, I=128, all 8 experts local, top-2, alignment
+                   64, routed scaling factor 2.5
+std_dsv3           standard single-GPU MoE of the DeepSeek-V3 shape: bf16
+                   input, 4096 rows, H=7168, I=2048, all 256 experts on
+                   the GPU (11 GB of fp8 weights), top-8 uniform,
+                   alignment 128, fp32 scales, routed scaling factor 2.5
+                   (the model's own)
 =================  =====================================================
 
 Recipe (numpy PCG64, seed 1000 + index): routing by Gumbel top-T over the
@@ -54,6 +62,8 @@ class Workload:
     src_ranks: int = 0      # >0: boundary given as a per-rank prefix sum
     tail_alias: bool = False
     seed: int = 1000
+    input: str = "fp8"      # 'fp8' (received, quantised) or 'bf16' (standard path)
+    routed_scale: float = 1.0   # routed scaling factor applied in the gather
     extra: dict = field(default_factory=dict)
 
 
@@ -71,6 +81,10 @@ WORKLOADS = {
                              tail_alias=True, seed=1004),
     "dsv3_local": Workload("dsv3_local", 4096, 7168, 2048, 8, 256, 8, 128,
                            routing="local", seed=1005),
+    "std_tiny": Workload("std_tiny", 64, 256, 128, 8, 8, 2, 64, seed=1006,
+                         input="bf16", routed_scale=2.5),
+    "std_dsv3": Workload("std_dsv3", 4096, 7168, 2048, 256, 256, 8, 128,
+                         seed=1007, input="bf16", routed_scale=2.5),
 }
 
 
