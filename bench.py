@@ -79,6 +79,27 @@ def quant_blocks(w, fmt):
     return q.view(E, N, K).view(torch.uint8).contiguous(), s.contiguous()
 
 
+def make_weights(wl, device, gen):
+    """w13 [E, 2I, H] and w2 [E, H, I] ~ N(0, 0.02), quantised per 128x128
+    block, drawn a few experts at a time (bounds the fp32 temporaries)."""
+    import torch
+    E, H, I = wl.experts, wl.hidden, wl.inter
+    sdt = torch.float32 if wl.fmt == "f32" else torch.uint8
+    w13q = torch.empty((E, 2 * I, H), dtype=torch.uint8, device=device)
+    w13s = torch.empty((E, 2 * I // 128, H // 128), dtype=sdt, device=device)
+    w2q = torch.empty((E, H, I), dtype=torch.uint8, device=device)
+    w2s = torch.empty((E, H // 128, I // 128), dtype=sdt, device=device)
+    step = 16
+    for e0 in range(0, E, step):
+        e1 = min(E, e0 + step)
+        t = torch.randn((e1 - e0, 2 * I, H), generator=gen, device=device) * 0.02
+        w13q[e0:e1], w13s[e0:e1] = quant_blocks(t, wl.fmt)
+        t = torch.randn((e1 - e0, H, I), generator=gen, device=device) * 0.02
+        w2q[e0:e1], w2s[e0:e1] = quant_blocks(t, wl.fmt)
+        del t
+    return w13q, w13s, w2q, w2s
+
+
 def make_inputs(wl, device):
     import numpy as np
     import torch
@@ -88,6 +109,14 @@ def make_inputs(wl, device):
     gen.manual_seed(wl.seed)
     R, H, I, E = wl.rows, wl.hidden, wl.inter, wl.experts
     x = torch.randn((R, H), generator=gen, device=device, dtype=torch.float32)
+    if wl.input == "bf16":      # standard path: bf16 token rows, quantised by the layout
+        xb = x.to(torch.bfloat16)
+        del x
+        w13q, w13s, w2q, w2s = make_weights(wl, device, gen)
+        torch.cuda.synchronize()
+        return dict(x=xb, x_scale=None, ids=torch.from_numpy(d["ids"]).to(device),
+                    w=torch.from_numpy(d["w"]).to(device), prank=None, w13=w13q,
+                    w13_scale=w13s, w2=w2q, w2_scale=w2s, num_valid=d["num_valid"], data=d)
     xq, xs = quant_rows(x, wl.fmt)
     del x
     nv = d["num_valid"]
@@ -98,12 +127,7 @@ def make_inputs(wl, device):
             bits = torch.randint(-2 ** 31, 2 ** 31 - 1, (R - nv, H // 128), generator=gen,
                                  device=device, dtype=torch.int32)
             xs[nv:] = bits.view(torch.float32)
-    w13 = torch.randn((E, 2 * I, H), generator=gen, device=device) * 0.02
-    w13q, w13s = quant_blocks(w13, wl.fmt)
-    del w13
-    w2 = torch.randn((E, H, I), generator=gen, device=device) * 0.02
-    w2q, w2s = quant_blocks(w2, wl.fmt)
-    del w2
+    w13q, w13s, w2q, w2s = make_weights(wl, device, gen)
     ids = torch.from_numpy(d["ids"]).to(device)
     wts = torch.from_numpy(d["w"]).to(device)
     prank = None
@@ -195,14 +219,22 @@ def main():
                           "bytes_written": dst.numel()}))
         return
     inp = make_inputs(wl, dev)
-    mod = M.ExpandedMoE(wl.rows, wl.topk, inp["w13"], inp["w13_scale"], inp["w2"],
-                        inp["w2_scale"], wl.align, wl.fmt, device=dev)
+    std = wl.input == "bf16"
+    if std:
+        mod = M.StandardMoE(wl.rows, wl.topk, inp["w13"], inp["w13_scale"], inp["w2"],
+                            inp["w2_scale"], wl.align, wl.fmt, wl.routed_scale, device=dev)
+    else:
+        mod = M.ExpandedMoE(wl.rows, wl.topk, inp["w13"], inp["w13_scale"], inp["w2"],
+                            inp["w2_scale"], wl.align, wl.fmt, device=dev)
     out = torch.empty((wl.rows, wl.hidden), dtype=torch.bfloat16, device=dev)
-    fold = mod.row_weight if wl.fmt == "f32" else None
+    fold = mod.row_weight if wl.fmt == "f32" and not std else None
 
     def stage(i):
         if i == 0:
-            mod.layout(inp["x"], inp["x_scale"], inp["ids"], inp["w"], inp["prank"])
+            if std:
+                mod.layout(inp["x"], inp["ids"], inp["w"])
+            else:
+                mod.layout(inp["x"], inp["x_scale"], inp["ids"], inp["w"], inp["prank"])
         elif i == 1:
             M.moe_grouped_gemm_fp8(mod.ex, mod.ex_scale, wl.fmt, mod.w13, mod.w13_scale,
                                    mod.psum, mod.status, wl.align, mod.gate_up)
@@ -308,8 +340,9 @@ def main():
     # kernel-trace summaries give the kernels' own durations).
     R, T, nv, E = wl.rows, wl.topk, inp["num_valid"], wl.experts
     sH, sI = (H // 128) * sb, (I // 128) * sb
+    row_in = 2 * H if std else H + sH   # a received row: bf16, or fp8 + scales
     st_bytes = {
-        "expand_layout": nv * T * 8 + A * (H + sH) + m_used * (H + sH + 4) + R * T * 4
+        "expand_layout": nv * T * 8 + A * row_in + m_used * (H + sH + 4) + R * T * 4
                          + mod.capacity * 4,
         "gemm_gate_up": g1_bytes,
         "act_quant": A * 4 * I + m_used * (I + sI),
@@ -329,7 +362,7 @@ def main():
         stages[n] = rec
 
     cpu = None
-    if not args.no_cpu_baseline:
+    if not args.no_cpu_baseline and not std:
         cpu = cpu_baseline(inp, wl, args.cpu_runs)
 
     res = {
@@ -345,7 +378,8 @@ def main():
         "vs_baseline": None,
         "dtype": "fp8_e4m3 (fp32 accumulate, bf16 out)",
         "data": "synthetic (seeded; routing/weights per the workload recipe)",
-        "config": {"workload": wl.name, "rows": wl.rows, "valid_rows": inp["num_valid"],
+        "config": {"workload": wl.name, "input": wl.input, "routed_scaling_factor": wl.routed_scale,
+                   "rows": wl.rows, "valid_rows": inp["num_valid"],
                    "hidden": H, "inter": I, "experts_local": wl.experts,
                    "experts_global": wl.global_experts, "topk": wl.topk,
                    "align": wl.align, "scale_fmt": wl.fmt, "parallelism": "ep-rank share, 1 GPU",

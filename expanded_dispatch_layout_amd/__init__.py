@@ -7,11 +7,14 @@ binding raises if the library is missing: there is no fallback.
 
 Functions mirror the C ABI in ``include/moe_expand.h``:
 
-    moe_expand_layout, moe_grouped_gemm_fp8, moe_act_quant, moe_gather,
-    moe_expand_capacity, moe_expand_workspace_bytes, moe_status_string
+    moe_expand_layout, moe_expand_layout_bf16, moe_grouped_gemm_fp8,
+    moe_act_quant, moe_gather, moe_expand_capacity, moe_expand_workspace_bytes,
+    moe_status_string
 
 plus :class:`ExpandedMoE`, which allocates the buffers once for a given
-receive-buffer size and runs the five calls of a layer in order.
+receive-buffer size and runs the five calls of a layer in order, and
+:class:`StandardMoE`, the same for the standard (non-EP) path: bf16 token
+rows in, top-k weights and the routed scaling factor applied in the gather.
 """
 
 import ctypes
@@ -39,10 +42,12 @@ _SIGNATURES = {
     "moe_expand_workspace_bytes": (_SZ, [_I64, _I, _I]),
     "moe_expand_layout": (_I, [_P, _I64, _P, _I64, _I, _P, _P, _P, _I, _I64, _I, _I,
                                _I, _I, _I64, _P, _P, _P, _P, _P, _P, _P, _P, _SZ, _P]),
+    "moe_expand_layout_bf16": (_I, [_P, _I64, _I, _P, _P, _P, _I, _I64, _I, _I, _I, _I,
+                                    _I64, _P, _P, _P, _P, _P, _P, _P, _P, _SZ, _P]),
     "moe_grouped_gemm_fp8": (_I, [_P, _P, _I, _P, _P, _P, _P, _I64, _I, _I, _I, _I,
                                   _P, _P]),
     "moe_act_quant": (_I, [_P, _P, _P, _P, _I64, _I, _I, _I, _I, _P, _P, _P, _P]),
-    "moe_gather": (_I, [_P, _P, _P, _P, _I, _I64, _I, _I, _I64, _P, _P]),
+    "moe_gather": (_I, [_P, _P, _P, ctypes.c_float, _P, _I, _I64, _I, _I, _I64, _P, _P]),
 }
 
 _lib = None
@@ -128,6 +133,23 @@ def moe_expand_layout(x, x_scale, fmt, topk_ids, topk_weights, psum_recv_per_ran
     _check("moe_expand_layout", code)
 
 
+def moe_expand_layout_bf16(x, fmt, topk_ids, topk_weights, psum_recv_per_rank,
+                           num_experts, align, capacity, ex, ex_scale, psum, m_indices,
+                           src2dst, row_weight, status, workspace, stream=None):
+    """x [rows, >=hidden] bf16 token rows, quantised per 1x128 group while
+    they are scattered; otherwise as moe_expand_layout."""
+    rows, hidden = topk_ids.shape[0], ex.shape[1]
+    code = lib().moe_expand_layout_bf16(
+        _ptr(x), x.stride(0), _fmt(fmt), _ptr(topk_ids), _ptr(topk_weights),
+        _ptr(psum_recv_per_rank),
+        0 if psum_recv_per_rank is None else psum_recv_per_rank.numel(),
+        rows, hidden, topk_ids.shape[1], num_experts, align, capacity,
+        _ptr(ex), _ptr(ex_scale), _ptr(psum), _ptr(m_indices), _ptr(src2dst),
+        _ptr(row_weight), _ptr(status), _ptr(workspace),
+        workspace.numel() * workspace.element_size(), _stream(stream))
+    _check("moe_expand_layout_bf16", code)
+
+
 def moe_grouped_gemm_fp8(a, a_scale, fmt, w, w_scale, psum, status, align, out,
                          stream=None):
     """a [capacity, k] fp8, a_scale [k/128, capacity], w [E, n, k] fp8,
@@ -151,12 +173,14 @@ def moe_act_quant(gate_up, m_indices, psum, status, num_experts, align, fmt, fol
     _check("moe_act_quant", code)
 
 
-def moe_gather(expert_out, src2dst, topk_weights, psum_recv_per_rank, out, stream=None):
+def moe_gather(expert_out, src2dst, topk_weights, psum_recv_per_rank, out, stream=None,
+               routed_scaling_factor=1.0):
     """expert_out [capacity, H] bf16, src2dst [rows, topk] -> out [rows, H] bf16."""
     rows, topk = src2dst.shape
     capacity, hidden = expert_out.shape
     code = lib().moe_gather(
-        _ptr(expert_out), _ptr(src2dst), _ptr(topk_weights), _ptr(psum_recv_per_rank),
+        _ptr(expert_out), _ptr(src2dst), _ptr(topk_weights), float(routed_scaling_factor),
+        _ptr(psum_recv_per_rank),
         0 if psum_recv_per_rank is None else psum_recv_per_rank.numel(),
         rows, hidden, topk, capacity, _ptr(out), _stream(stream))
     _check("moe_gather", code)
@@ -225,6 +249,46 @@ class ExpandedMoE:
         if out is None:
             out = torch.empty((self.rows, self.H), dtype=torch.bfloat16, device=x.device)
         self.layout(x, x_scale, topk_ids, topk_weights, psum_recv_per_rank, stream)
+        self.experts(stream)
+        self.gather(topk_weights, psum_recv_per_rank, out, stream)
+        return out
+
+
+class StandardMoE(ExpandedMoE):
+    """The standard (non-EP) path: bf16 token rows (every expert local) are
+    quantised per 1x128 group while they are scattered into the 128-aligned
+    expert blocks; the same GEMMs and activation run with no weight fold;
+    the gather applies the top-k weights and the routed scaling factor."""
+
+    def __init__(self, rows, topk, w13, w13_scale, w2, w2_scale, align=128, fmt="f32",
+                 routed_scaling_factor=1.0, device="cuda"):
+        super().__init__(rows, topk, w13, w13_scale, w2, w2_scale, align, fmt, device)
+        self.routed_scaling_factor = float(routed_scaling_factor)
+
+    def layout(self, x, topk_ids, topk_weights, psum_recv_per_rank=None, stream=None):
+        moe_expand_layout_bf16(x, self.fmt, topk_ids, topk_weights, psum_recv_per_rank,
+                               self.E, self.align, self.capacity, self.ex, self.ex_scale,
+                               self.psum, self.m_indices, self.src2dst, None, self.status,
+                               self.workspace, stream)
+
+    def experts(self, stream=None):
+        moe_grouped_gemm_fp8(self.ex, self.ex_scale, self.fmt, self.w13, self.w13_scale,
+                             self.psum, self.status, self.align, self.gate_up, stream)
+        moe_act_quant(self.gate_up, self.m_indices, self.psum, self.status, self.E,
+                      self.align, self.fmt, None, self.dq, self.ds, stream)
+        moe_grouped_gemm_fp8(self.dq, self.ds, self.fmt, self.w2, self.w2_scale,
+                             self.psum, self.status, self.align, self.down, stream)
+
+    def gather(self, topk_weights, psum_recv_per_rank, out, stream=None):
+        moe_gather(self.down, self.src2dst, topk_weights, psum_recv_per_rank, out, stream,
+                   routed_scaling_factor=self.routed_scaling_factor)
+
+    def __call__(self, x, topk_ids, topk_weights, psum_recv_per_rank=None, out=None,
+                 stream=None):
+        import torch
+        if out is None:
+            out = torch.empty((self.rows, self.H), dtype=torch.bfloat16, device=x.device)
+        self.layout(x, topk_ids, topk_weights, psum_recv_per_rank, stream)
         self.experts(stream)
         self.gather(topk_weights, psum_recv_per_rank, out, stream)
         return out

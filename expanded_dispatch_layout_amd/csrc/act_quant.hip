@@ -26,13 +26,6 @@ __device__ __forceinline__ float silu_mul(float g, float u) {
   return __fmul_rn(__fdiv_rn(g, den), u);
 }
 
-__device__ __forceinline__ uint32_t e8m0_round_up(float s) {
-  const uint32_t bits = __float_as_uint(s);
-  const uint32_t ex = bits >> 23, mant = bits & 0x7fffffu;
-  const bool bump = (mant > 0) && (ex != 0xfe) && !(ex == 0 && mant <= 0x400000u);
-  return ex + (bump ? 1u : 0u);
-}
-
 template <bool kUe8m0, bool kFold>
 __global__ __launch_bounds__(kThreads) void act_quant_kernel(
     const uint16_t* __restrict__ gu, const int32_t* __restrict__ m_indices,

@@ -62,4 +62,16 @@ __device__ __forceinline__ float bf16_to_f32(uint16_t h) {
   return __uint_as_float(((uint32_t)h) << 16);
 }
 
+// UE8M0 byte of the smallest power of two not below the fp32 scale s: the
+// biased exponent, plus one unless the mantissa is zero; the largest finite
+// exponent is not bumped, and neither is a denormal of at most half the
+// smallest normal (SGLang moe_runner/deep_gemm.py source,
+// _cast_to_e8m0_with_rounding_up).
+__device__ __forceinline__ uint32_t e8m0_round_up(float s) {
+  const uint32_t bits = __float_as_uint(s);
+  const uint32_t ex = bits >> 23, mant = bits & 0x7fffffu;
+  const bool bump = (mant > 0) && (ex != 0xfe) && !(ex == 0 && mant <= 0x400000u);
+  return ex + (bump ? 1u : 0u);
+}
+
 }  // namespace moe

@@ -4,12 +4,15 @@
 // deepep_v2 (expanded branch: rows weighted, then combined) and ep_gather's
 // use in post_permute_deep_gemm_to_deepep_normal; SGLang PR 37261
 // Modifications/Core (under UE8M0 scales the top-k weight is applied to the
-// down output rather than folded into the scale).
+// down output rather than folded into the scale); the standard path's
+// post_permute_deep_gemm_to_standard (post_reorder_deepgemm: the top-k
+// weighted sum times the routed scaling factor).
 //
 // Four token rows per workgroup; each thread owns up to four 16-byte chunks
 // (8 bf16 each) of a row.  The slots are summed in ascending k, each
-// product and sum rounded to fp32 (no contraction), with one bf16 rounding at
-// the end.  HBM-bound: reads A rows of expert output, writes R_v token rows
+// product and sum rounded to fp32 (no contraction), the sum multiplied by the
+// routed scaling factor (1 on the expand path: exact), with one bf16 rounding
+// at the end.  HBM-bound: reads A rows of expert output, writes R_v token rows
 // (non-temporal stores: the output is not re-read by this layer).
 #include "common.hpp"
 
@@ -35,10 +38,10 @@ __device__ __forceinline__ void acc8(float* a, const u32x4& v, float c, bool wei
 
 constexpr int kRowsPerBlock = 4;  // one wave reads each row's slot list
 
-// Zero-route rows, fp32 accumulation of row r's live slots (its n slots at
-// dsts / ws), bf16 rounding once, non-temporal 16-byte stores.
+// Row r's fp32 sums (zeros for a row without a live slot) times `scale`,
+// rounded once to bf16, non-temporal 16-byte stores.
 __device__ __forceinline__ void store_row(uint16_t* __restrict__ out, int64_t r, int hidden,
-                                          const float (&a)[kChunksPerThread][8]) {
+                                          const float (&a)[kChunksPerThread][8], float scale) {
   const int t = threadIdx.x, nch = hidden / 8;
   u32x4* orow = reinterpret_cast<u32x4*>(out + r * hidden);
 #pragma unroll
@@ -48,8 +51,8 @@ __device__ __forceinline__ void store_row(uint16_t* __restrict__ out, int64_t r,
       u32x4 o;
 #pragma unroll
       for (int j = 0; j < 4; ++j)
-        o[j] = (uint32_t)f32_to_bf16_rne(a[i][2 * j]) |
-               ((uint32_t)f32_to_bf16_rne(a[i][2 * j + 1]) << 16);
+        o[j] = (uint32_t)f32_to_bf16_rne(__fmul_rn(a[i][2 * j], scale)) |
+               ((uint32_t)f32_to_bf16_rne(__fmul_rn(a[i][2 * j + 1], scale)) << 16);
       __builtin_nontemporal_store(o, orow + c);
     }
   }
@@ -65,8 +68,8 @@ __device__ __forceinline__ void store_row(uint16_t* __restrict__ out, int64_t r,
 // contraction).
 __global__ __launch_bounds__(kThreads) void gather_kernel(
     const uint16_t* __restrict__ eo, const int32_t* __restrict__ src2dst,
-    const float* __restrict__ topk_w, const int32_t* __restrict__ psum_rank, int nsrc,
-    int64_t rows, int hidden, int topk, int64_t capacity, uint16_t* __restrict__ out) {
+    const float* __restrict__ topk_w, float scale, const int32_t* __restrict__ psum_rank,
+    int nsrc, int64_t rows, int hidden, int topk, int64_t capacity, uint16_t* __restrict__ out) {
   __shared__ int l_dst[kRowsPerBlock][MOE_MAX_TOPK];
   __shared__ float l_w[kRowsPerBlock][MOE_MAX_TOPK];
   __shared__ int l_n[kRowsPerBlock];
@@ -124,7 +127,7 @@ __global__ __launch_bounds__(kThreads) void gather_kernel(
 #pragma unroll
       for (int j = 0; j < 8; ++j) a[i][j] = 0.f;
     for (int j = 0; j < kRowsPerBlock; ++j)
-      if (l_n[j] == 0) store_row(out, r0 + j, hidden, a);
+      if (l_n[j] == 0) store_row(out, r0 + j, hidden, a, 1.f);
     // Rows with live slots.
     for (int j = (jl >= 0 ? jl : kRowsPerBlock); j < kRowsPerBlock; ++j) {
       const int n = l_n[j];
@@ -144,7 +147,7 @@ __global__ __launch_bounds__(kThreads) void gather_kernel(
           }
         }
       }
-      store_row(out, r0 + j, hidden, a);
+      store_row(out, r0 + j, hidden, a, scale);
     }
     __syncthreads();  // the slot lists are rewritten for the next quad
   }
@@ -156,7 +159,8 @@ __global__ __launch_bounds__(kThreads) void gather_kernel(
 using namespace moe;
 
 extern "C" moe_status moe_gather(const void* expert_out, const int32_t* src2dst,
-                                 const float* topk_weights, const int32_t* psum_recv_per_rank,
+                                 const float* topk_weights, float routed_scaling_factor,
+                                 const int32_t* psum_recv_per_rank,
                                  int num_src_ranks, int64_t rows, int hidden, int topk,
                                  int64_t capacity, void* out, void* stream) {
   if (rows < 0 || hidden <= 0 || hidden % kGroup != 0 || topk < 1 || topk > MOE_MAX_TOPK ||
@@ -164,6 +168,9 @@ extern "C" moe_status moe_gather(const void* expert_out, const int32_t* src2dst,
     return MOE_ERR_SHAPE;
   if (num_src_ranks < 0 || (psum_recv_per_rank && num_src_ranks == 0)) return MOE_ERR_SHAPE;
   if (rows > 0 && (!src2dst || !out)) return MOE_ERR_NULL;
+  if (!(routed_scaling_factor == routed_scaling_factor) ||
+      __builtin_isinf(routed_scaling_factor))
+    return MOE_ERR_UNSUPPORTED;  // a NaN or infinite factor
   if (capacity > 0 && !expert_out) return MOE_ERR_NULL;
   if (((uintptr_t)expert_out % 16) || ((uintptr_t)out % 16)) return MOE_ERR_ALIGNMENT;
   if (hidden / 8 > kThreads * kChunksPerThread) return MOE_ERR_UNSUPPORTED;
@@ -174,7 +181,8 @@ extern "C" moe_status moe_gather(const void* expert_out, const int32_t* src2dst,
   const int64_t quads = (rows + kRowsPerBlock - 1) / kRowsPerBlock;
   const int64_t grid = quads < 1024 ? quads : 1024;
   hipLaunchKernelGGL(gather_kernel, dim3((unsigned)grid), dim3(kThreads), 0, s,
-                     (const uint16_t*)expert_out, src2dst, topk_weights, psum_recv_per_rank,
+                     (const uint16_t*)expert_out, src2dst, topk_weights, routed_scaling_factor,
+                     psum_recv_per_rank,
                      num_src_ranks, rows, hidden, topk, capacity, (uint16_t*)out);
   if (hipGetLastError() != hipSuccess) return MOE_ERR_LAUNCH;
   return MOE_OK;

@@ -29,6 +29,13 @@
 //             read once and written to each destination.  The same grid
 //             zero-fills the alignment pad rows and writes the row labels
 //             (grid-stride), so no extra pass is needed.
+//
+// bf16 input (the standard path, SGLang moe_runner/deep_gemm.py source,
+// pre_permute_standard_to_deep_gemm: per-token-group quantisation, then the
+// scatter): the same kernels; the scatter reads each bf16 row once,
+// quantises it per 1x128 group in registers (16 lanes per group, max by
+// xor-shuffles) and writes the codes and the group scales to every
+// destination, so the quantised rows never make a round trip through HBM.
 #include "common.hpp"
 
 namespace moe {
@@ -274,13 +281,15 @@ struct RowFetch {
     mine = myid >= 0 && myid < E;
     live = __ballot(mine);
   }
+  // kQ: the row is bf16 (2 bytes per element) and has no scales.
+  template <bool kQ>
   __device__ __forceinline__ void data_of(const uint8_t* __restrict__ x, int64_t x_stride,
                                           const uint8_t* __restrict__ x_scale,
                                           int64_t x_scale_stride_bytes, int scale_bytes,
                                           const float* __restrict__ topk_w,
                                           const int32_t* __restrict__ grp_off, bool weights,
                                           int64_t r, int hidden, int topk, int E, int lane) {
-    const int nch = hidden / 16, nsc = hidden / kGroup;
+    const int nch = kQ ? hidden / 8 : hidden / 16, nsc = hidden / kGroup;
     const u32x4* src = reinterpret_cast<const u32x4*>(x + r * x_stride);
     const uint8_t* srow = x_scale + r * x_scale_stride_bytes;
 #pragma unroll
@@ -290,7 +299,7 @@ struct RowFetch {
     }
     sf = 0.f;
     sb = 0;
-    if (lane < nsc) {
+    if (!kQ && lane < nsc) {
       if (scale_bytes == 4) sf = reinterpret_cast<const float*>(srow)[lane];
       else sb = srow[lane];
     }
@@ -303,6 +312,54 @@ struct RowFetch {
   }
 };
 
+// One pass of a bf16 row (chunk c = c0 + u * 64 + lane, 8 elements each)
+// quantised per 1x128 group: the 16 lanes of a group share its amax; codes
+// (8 bytes per chunk) and the group's scale (fp32, or the UE8M0 byte in the
+// low bits) per u.  Inactive chunks (c >= nch) give amax 0 and are not
+// stored by the caller.  Every lane runs the shuffles.
+template <bool kUe8m0>
+__device__ __forceinline__ void quant_pass(const u32x4 (&v)[8], int c0, int nch, int lane,
+                                           uint2 (&q)[8], uint32_t (&sc)[8]) {
+#pragma unroll
+  for (int u = 0; u < 8; ++u) {
+    const bool active = c0 + u * 64 + lane < nch;
+    float y[8];
+    float amax = 0.f;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      y[2 * i] = __uint_as_float(v[u][i] << 16);
+      y[2 * i + 1] = __uint_as_float(v[u][i] & 0xffff0000u);
+    }
+    if (active) {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) amax = fmaxf(amax, fabsf(y[i]));
+    }
+#pragma unroll
+    for (int o = 8; o > 0; o >>= 1) amax = fmaxf(amax, __shfl_xor(amax, o, 64));
+    amax = fmaxf(amax, 1e-10f);
+    float p[8];
+    if (kUe8m0) {
+      const uint32_t b = e8m0_round_up(__fdiv_rn(amax, 448.0f));
+#pragma unroll
+      for (int i = 0; i < 8; ++i) p[i] = ldexpf(y[i], 127 - (int)b);
+      sc[u] = b;
+    } else {
+      const float inv = __fdiv_rn(448.0f, amax);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) p[i] = __fmul_rn(y[i], inv);
+      sc[u] = __float_as_uint(__fdiv_rn(amax, 448.0f));
+    }
+    int lo = __builtin_amdgcn_cvt_pk_fp8_f32(p[0], p[1], 0, false);
+    lo = __builtin_amdgcn_cvt_pk_fp8_f32(p[2], p[3], lo, true);
+    int hi = __builtin_amdgcn_cvt_pk_fp8_f32(p[4], p[5], 0, false);
+    hi = __builtin_amdgcn_cvt_pk_fp8_f32(p[6], p[7], hi, true);
+    q[u] = make_uint2((uint32_t)lo, (uint32_t)hi);
+  }
+}
+
+// kQ: bf16 input rows quantised here (x_scale unused); otherwise fp8 rows
+// and their scales are copied.
+template <bool kQ>
 __global__ __launch_bounds__(kScatterThreads) void expand_scatter_kernel(
     const uint8_t* __restrict__ x, int64_t x_stride, const uint8_t* __restrict__ x_scale,
     int64_t x_scale_stride_bytes, int scale_bytes, const int32_t* __restrict__ ids,
@@ -340,8 +397,8 @@ __global__ __launch_bounds__(kScatterThreads) void expand_scatter_kernel(
   // costs nothing, whereas after the row's loads the wait would cover them.
   if (t < nbe) l_blk[t] = blk0;
   if (wave0 < rows && f.live)
-    f.data_of(x, x_stride, x_scale, x_scale_stride_bytes, scale_bytes, topk_w, grp_off,
-              row_weight != nullptr, wave0, hidden, topk, E, lane);
+    f.data_of<kQ>(x, x_stride, x_scale, x_scale_stride_bytes, scale_bytes, topk_w, grp_off,
+                  row_weight != nullptr, wave0, hidden, topk, E, lane);
   const int32_t* blk_off;  // exclusive per-block offsets, [nblk][E]
   if (fold) {
     // The scan over the (few) block totals, done by every workgroup: block
@@ -428,15 +485,16 @@ __global__ __launch_bounds__(kScatterThreads) void expand_scatter_kernel(
   const int total = l_total;
   const int64_t nrows_ex = min((int64_t)total, capacity);
   const int nsc = hidden / kGroup;
-  const int nch = hidden / 16;
+  const int nch = hidden / 16;                     // 16-byte chunks of an expanded row
+  const int nch_in = kQ ? hidden / 8 : nch;        // ... of a received row
 
   // ---- one wave per received row ----
   for (int64_t r = wave0; r < rows; r += gwaves) {
     if (r != wave0) {
       f.ids_of(ids, r, nv, topk, E, lane);
       if (f.live)
-        f.data_of(x, x_stride, x_scale, x_scale_stride_bytes, scale_bytes, topk_w, grp_off,
-                  row_weight != nullptr, r, hidden, topk, E, lane);
+        f.data_of<kQ>(x, x_stride, x_scale, x_scale_stride_bytes, scale_bytes, topk_w, grp_off,
+                      row_weight != nullptr, r, hidden, topk, E, lane);
     }
     if (f.live == 0) {
       if (lane < topk) src2dst[r * topk + lane] = -1;
@@ -468,13 +526,39 @@ __global__ __launch_bounds__(kScatterThreads) void expand_scatter_kernel(
     if (mask == 0) continue;
     const u32x4* src = reinterpret_cast<const u32x4*>(x + r * x_stride);
     const uint8_t* srow = x_scale + r * x_scale_stride_bytes;
-    for (int c0 = 0; c0 < nch; c0 += 64 * 8) {
+    for (int c0 = 0; c0 < nch_in; c0 += 64 * 8) {
       if (c0 > 0) {
 #pragma unroll
         for (int u = 0; u < 8; ++u) {
           const int c = c0 + u * 64 + lane;
-          if (c < nch) f.v[u] = src[c];
+          if (c < nch_in) f.v[u] = src[c];
         }
+      }
+      if constexpr (kQ) {
+        // Quantise the pass once, then store it to every destination: the
+        // codes of chunk c at byte 8c of the expanded row, the scale of group
+        // c / 16 (K-block-major) from the group's first lane.
+        uint2 q[8];
+        uint32_t sc[8];
+        if (scale_bytes == 1) quant_pass<true>(f.v, c0, nch_in, lane, q, sc);
+        else quant_pass<false>(f.v, c0, nch_in, lane, q, sc);
+        for (uint64_t mm = mask; mm; mm &= mm - 1) {
+          const int dk = __shfl(d, __builtin_ctzll(mm), 64);
+          uint2* dst = reinterpret_cast<uint2*>(ex + (int64_t)dk * hidden);
+#pragma unroll
+          for (int u = 0; u < 8; ++u) {
+            const int c = c0 + u * 64 + lane;
+            if (c < nch_in) {
+              dst[c] = q[u];
+              if ((lane & 15) == 0) {
+                const int64_t at = (int64_t)(c >> 4) * capacity + dk;
+                if (scale_bytes == 4) reinterpret_cast<uint32_t*>(ex_scale)[at] = sc[u];
+                else ex_scale[at] = (uint8_t)sc[u];
+              }
+            }
+          }
+        }
+        continue;
       }
       for (uint64_t mm = mask; mm; mm &= mm - 1) {
         const int dk = __shfl(d, __builtin_ctzll(mm), 64);
@@ -486,6 +570,7 @@ __global__ __launch_bounds__(kScatterThreads) void expand_scatter_kernel(
         }
       }
     }
+    if constexpr (kQ) continue;  // the scales were written with the codes
     // Scales: the shuffles run with every lane active (a lane-divergent
     // shuffle could read an inactive lane), the stores only where c < nsc.
     for (int c0 = 0; c0 < nsc; c0 += 64) {
@@ -543,13 +628,18 @@ extern "C" size_t moe_expand_workspace_bytes(int64_t rows, int topk, int num_exp
   return workspace_bytes(rows, num_experts);
 }
 
-extern "C" moe_status moe_expand_layout(
-    const void* x, int64_t x_stride, const void* x_scale, int64_t x_scale_stride,
-    moe_scale_fmt fmt, const int32_t* topk_ids, const float* topk_weights,
-    const int32_t* psum_recv_per_rank, int num_src_ranks, int64_t rows, int hidden, int topk,
-    int num_experts, int align, int64_t capacity, void* ex, void* ex_scale, int32_t* psum,
-    int32_t* m_indices, int32_t* src2dst, float* row_weight, int32_t* status, void* workspace,
-    size_t workspace_bytes_, void* stream) {
+namespace {
+
+// Both entry points.  bf16: x holds bf16 rows, x_stride is in bytes here,
+// x_scale is unused.
+moe_status expand_layout(bool bf16, const void* x, int64_t x_stride, const void* x_scale,
+                         int64_t x_scale_stride, moe_scale_fmt fmt, const int32_t* topk_ids,
+                         const float* topk_weights, const int32_t* psum_recv_per_rank,
+                         int num_src_ranks, int64_t rows, int hidden, int topk, int num_experts,
+                         int align, int64_t capacity, void* ex, void* ex_scale, int32_t* psum,
+                         int32_t* m_indices, int32_t* src2dst, float* row_weight,
+                         int32_t* status, void* workspace, size_t workspace_bytes_,
+                         void* stream) {
   if (rows < 0 || hidden <= 0 || hidden % kGroup != 0 || topk < 1 || topk > MOE_MAX_TOPK ||
       num_experts < 1 || num_experts > MOE_MAX_EXPERTS || capacity < 0 || rows > (1LL << 30) ||
       capacity > (1LL << 30) || (int64_t)rows * topk > (1LL << 30))
@@ -558,10 +648,12 @@ extern "C" moe_status moe_expand_layout(
     return MOE_ERR_UNSUPPORTED;
   if (capacity % align != 0) return MOE_ERR_SHAPE;
   if (fmt != MOE_SCALE_F32 && fmt != MOE_SCALE_UE8M0) return MOE_ERR_UNSUPPORTED;
-  if (x_stride < hidden || x_scale_stride < hidden / kGroup) return MOE_ERR_SHAPE;
+  if (x_stride < (bf16 ? 2 * (int64_t)hidden : hidden) ||
+      (!bf16 && x_scale_stride < hidden / kGroup))
+    return MOE_ERR_SHAPE;
   if (num_src_ranks < 0 || (psum_recv_per_rank && num_src_ranks == 0)) return MOE_ERR_SHAPE;
   if (!psum || !m_indices || !src2dst || !status) return MOE_ERR_NULL;
-  if (rows > 0 && (!x || !x_scale || !topk_ids)) return MOE_ERR_NULL;
+  if (rows > 0 && (!x || (!bf16 && !x_scale) || !topk_ids)) return MOE_ERR_NULL;
   if (capacity > 0 && (!ex || !ex_scale)) return MOE_ERR_NULL;
   if (row_weight && !topk_weights && rows > 0) return MOE_ERR_NULL;
   if ((x_stride % 16) || ((uintptr_t)x % 16) || ((uintptr_t)ex % 16)) return MOE_ERR_ALIGNMENT;
@@ -600,7 +692,8 @@ extern "C" moe_status moe_expand_layout(
   if (grid < 1024) grid = 1024;
   if (grid > 16384) grid = 16384;
   const size_t lds = (size_t(4) * E + 1 + (fold ? size_t(nb) * E : 0)) * 4;
-  hipLaunchKernelGGL(expand_scatter_kernel, dim3((unsigned)grid), dim3(kScatterThreads), lds, s,
+  hipLaunchKernelGGL(bf16 ? expand_scatter_kernel<true> : expand_scatter_kernel<false>,
+                     dim3((unsigned)grid), dim3(kScatterThreads), lds, s,
                      (const uint8_t*)x, x_stride, (const uint8_t*)x_scale,
                      x_scale_stride * scale_bytes, scale_bytes, topk_ids, topk_weights,
                      psum_recv_per_rank, num_src_ranks, rows, hidden, topk, E, capacity, align,
@@ -609,4 +702,32 @@ extern "C" moe_status moe_expand_layout(
                      row_weight);
   if (hipGetLastError() != hipSuccess) return MOE_ERR_LAUNCH;
   return MOE_OK;
+}
+
+}  // namespace
+
+extern "C" moe_status moe_expand_layout(
+    const void* x, int64_t x_stride, const void* x_scale, int64_t x_scale_stride,
+    moe_scale_fmt fmt, const int32_t* topk_ids, const float* topk_weights,
+    const int32_t* psum_recv_per_rank, int num_src_ranks, int64_t rows, int hidden, int topk,
+    int num_experts, int align, int64_t capacity, void* ex, void* ex_scale, int32_t* psum,
+    int32_t* m_indices, int32_t* src2dst, float* row_weight, int32_t* status, void* workspace,
+    size_t workspace_bytes_, void* stream) {
+  return expand_layout(false, x, x_stride, x_scale, x_scale_stride, fmt, topk_ids, topk_weights,
+                       psum_recv_per_rank, num_src_ranks, rows, hidden, topk, num_experts, align,
+                       capacity, ex, ex_scale, psum, m_indices, src2dst, row_weight, status,
+                       workspace, workspace_bytes_, stream);
+}
+
+extern "C" moe_status moe_expand_layout_bf16(
+    const void* x, int64_t x_stride, moe_scale_fmt fmt, const int32_t* topk_ids,
+    const float* topk_weights, const int32_t* psum_recv_per_rank, int num_src_ranks,
+    int64_t rows, int hidden, int topk, int num_experts, int align, int64_t capacity, void* ex,
+    void* ex_scale, int32_t* psum, int32_t* m_indices, int32_t* src2dst, float* row_weight,
+    int32_t* status, void* workspace, size_t workspace_bytes_, void* stream) {
+  if (x_stride < 0 || x_stride > (1LL << 40)) return MOE_ERR_SHAPE;
+  return expand_layout(true, x, x_stride * 2, nullptr, 0, fmt, topk_ids, topk_weights,
+                       psum_recv_per_rank, num_src_ranks, rows, hidden, topk, num_experts, align,
+                       capacity, ex, ex_scale, psum, m_indices, src2dst, row_weight, status,
+                       workspace, workspace_bytes_, stream);
 }

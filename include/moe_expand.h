@@ -18,6 +18,12 @@
  *   moe_gather            each token's expert rows summed back into one
  *                          bf16 row (weighted here under UE8M0 scales)
  *
+ * The standard (non-EP) path [P3 pre_permute_standard_to_deep_gemm,
+ * post_permute_deep_gemm_to_standard] uses the same calls, entering with
+ * moe_expand_layout_bf16 (bf16 token rows, quantised per 1x128 group while
+ * they are scattered) and leaving through moe_gather with the top-k weights
+ * and the routed scaling factor.
+ *
  * Sources, by page and section:
  *  [P1] SGLang pull request 37261, "feat(deepep_v2): expanded (do_expand=True)
  *       prefill dispatch for DeepEP-V2": Modifications/Core (row labels from
@@ -36,7 +42,11 @@
  *       (gate_up GEMM, SiLU*up, per-token-group fp8 quant, down GEMM),
  *       _get_compact_all_tokens (capacity bound), _cast_to_e8m0_with_
  *       rounding_up (UE8M0 rule), pre_permute_deepep_v2_to_deep_gemm and
- *       post_permute_deep_gemm_to_deepep_v2 (expanded branch).
+ *       post_permute_deep_gemm_to_deepep_v2 (expanded branch),
+ *       pre_permute_standard_to_deep_gemm (bf16 rows quantised per token
+ *       group, then scattered into 128-aligned expert blocks) and
+ *       post_permute_deep_gemm_to_standard (top-k weights and the routed
+ *       scaling factor in the reduction).
  *
  * Conventions for every call:
  *  - Pointers named as device buffers are device memory the caller owns
@@ -167,6 +177,34 @@ moe_status moe_expand_layout(
     void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * Expanded layout of bf16 token rows, quantised on the way [P3
+ * pre_permute_standard_to_deep_gemm: per-token-group fp8 quantisation of the
+ * hidden states, then the scatter into the aligned expert blocks].
+ *
+ * As moe_expand_layout, except:
+ *   x          [rows, x_stride] bf16 token rows (x_stride in elements,
+ *              >= hidden; x_stride * 2 % 16 == 0, x 16-byte aligned); there
+ *              is no x_scale.  Each valid row with a live slot is read once,
+ *              quantised per 1x128 group and written to every destination:
+ *                amax = max(max |x| over the group, 1e-10)
+ *                fp32:  scale = amax / 448, q = fp8_rne(x * (448 / amax))
+ *                UE8M0: b = smallest exponent byte with 2^(b-127) >= amax/448,
+ *                       q = fp8_rne(x * 2^(127-b))
+ *              (each operation rounded in fp32; the same rule as
+ *              moe_act_quant's).  Rows without a live slot are not read.
+ * Errors, ownership and every other argument: as moe_expand_layout.
+ */
+moe_status moe_expand_layout_bf16(
+    const void* x, int64_t x_stride, moe_scale_fmt fmt,
+    const int32_t* topk_ids, const float* topk_weights,
+    const int32_t* psum_recv_per_rank, int num_src_ranks,
+    int64_t rows, int hidden, int topk, int num_experts, int align,
+    int64_t capacity,
+    void* ex, void* ex_scale, int32_t* psum, int32_t* m_indices,
+    int32_t* src2dst, float* row_weight, int32_t* status,
+    void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * Contiguous grouped fp8 GEMM, "NT": out[m, :] = A[m, :] . W[e]^T for every
  * expanded row m of expert e [P3 _run_contiguous_gemm; P1 Core].
  *
@@ -226,24 +264,29 @@ moe_status moe_act_quant(
 /*
  * Weighted gather back to token rows [P3 post_permute_deep_gemm_to_deepep_v2
  * and ep_gather's use in post_permute_deep_gemm_to_deepep_normal; P1 Core
- * (UE8M0 weighting of the down output)].
+ * (UE8M0 weighting of the down output); P3 post_permute_deep_gemm_to_standard
+ * (the routed scaling factor)].
  *
  *   expert_out   [capacity, hidden] bf16 (down projection output)
  *   src2dst      [rows, topk] int32 as written by moe_expand_layout;
  *                entries outside [0, capacity) are treated as -1
  *   topk_weights [rows, topk] fp32, or NULL when the weights were folded
+ *   routed_scaling_factor  multiplies each row's sum (1 on the expand path;
+ *                the model's factor on the standard path); a NaN or infinite
+ *                factor is MOE_ERR_UNSUPPORTED
  *   psum_recv_per_rank / num_src_ranks  as for the layout (R_v)
  *   out          [rows, hidden] bf16
- * For r < R_v: out[r] = bf16( sum over k ascending with src2dst[r,k] >= 0 of
- *   c_k * float(expert_out[src2dst[r,k]]) ), c_k = topk_weights[r,k] or 1,
- * each product and sum rounded to fp32 in that order.  Valid rows with no
- * live slot become 0.  Rows >= R_v are not written.
+ * For r < R_v: out[r] = bf16( f * sum over k ascending with src2dst[r,k] >= 0
+ *   of c_k * float(expert_out[src2dst[r,k]]) ), c_k = topk_weights[r,k] or 1,
+ * f = routed_scaling_factor, each product and sum rounded to fp32 in that
+ * order.  Valid rows with no live slot become 0.  Rows >= R_v are not
+ * written.
  * Sizes: hidden % 128 == 0 and hidden <= 8192 (else MOE_ERR_UNSUPPORTED);
  * buffers 16-byte aligned.
  */
 moe_status moe_gather(
     const void* expert_out, const int32_t* src2dst, const float* topk_weights,
-    const int32_t* psum_recv_per_rank, int num_src_ranks,
+    float routed_scaling_factor, const int32_t* psum_recv_per_rank, int num_src_ranks,
     int64_t rows, int hidden, int topk, int64_t capacity,
     void* out, void* stream);
 

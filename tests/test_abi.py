@@ -20,7 +20,8 @@ MIS = FAKE + 4           # misaligned
 
 def test_library_exports_every_header_function():
     names = M.header_functions()
-    assert set(names) >= {"moe_expand_layout", "moe_grouped_gemm_fp8", "moe_act_quant",
+    assert set(names) >= {"moe_expand_layout", "moe_expand_layout_bf16",
+                          "moe_grouped_gemm_fp8", "moe_act_quant",
                           "moe_gather", "moe_expand_capacity",
                           "moe_expand_workspace_bytes", "moe_status_string"}
     lib = M.lib()
@@ -128,15 +129,42 @@ def test_act_quant_rejects_bad_arguments():
     assert call(cap=0) == M.MOE_OK
 
 
+def _layout_bf16(**kw):
+    a = dict(x=FAKE, x_stride=256, fmt=0, ids=FAKE, w=FAKE, prank=None, nsrc=0, rows=64,
+             hidden=256, topk=2, E=4, align=64, cap=320, ex=FAKE, exs=FAKE, psum=FAKE,
+             mi=FAKE, s2d=FAKE, rw=None, st=FAKE, ws=FAKE, wsb=0, stream=None)
+    a.update(kw)
+    return M.lib().moe_expand_layout_bf16(
+        a["x"], a["x_stride"], a["fmt"], a["ids"], a["w"], a["prank"], a["nsrc"], a["rows"],
+        a["hidden"], a["topk"], a["E"], a["align"], a["cap"], a["ex"], a["exs"], a["psum"],
+        a["mi"], a["s2d"], a["rw"], a["st"], a["ws"], a["wsb"], a["stream"])
+
+
+def test_layout_bf16_rejects_bad_arguments():
+    assert _layout_bf16(hidden=100) == M.MOE_ERR_SHAPE
+    assert _layout_bf16(x_stride=128) == M.MOE_ERR_SHAPE      # < hidden elements
+    assert _layout_bf16(x_stride=-1) == M.MOE_ERR_SHAPE
+    assert _layout_bf16(x_stride=260) == M.MOE_ERR_ALIGNMENT  # 520 bytes: not 16-aligned
+    assert _layout_bf16(x=MIS) == M.MOE_ERR_ALIGNMENT
+    assert _layout_bf16(x=None) == M.MOE_ERR_NULL
+    assert _layout_bf16(fmt=3) == M.MOE_ERR_UNSUPPORTED
+    assert _layout_bf16(align=48) == M.MOE_ERR_UNSUPPORTED
+    assert _layout_bf16(rw=FAKE, w=None) == M.MOE_ERR_NULL
+    assert _layout_bf16(ws=None) == M.MOE_ERR_WORKSPACE
+    assert _layout_bf16(wsb=16) == M.MOE_ERR_WORKSPACE       # everything else valid
+
+
 def test_gather_rejects_bad_arguments():
     f = M.lib().moe_gather
 
     def call(**kw):
-        a = dict(eo=FAKE, s2d=FAKE, w=None, prank=None, nsrc=0, rows=64, hidden=256,
-                 topk=2, cap=320, out=FAKE)
+        a = dict(eo=FAKE, s2d=FAKE, w=None, scale=1.0, prank=None, nsrc=0, rows=64,
+                 hidden=256, topk=2, cap=320, out=FAKE)
         a.update(kw)
-        return f(a["eo"], a["s2d"], a["w"], a["prank"], a["nsrc"], a["rows"], a["hidden"],
-                 a["topk"], a["cap"], a["out"], None)
+        return f(a["eo"], a["s2d"], a["w"], a["scale"], a["prank"], a["nsrc"], a["rows"],
+                 a["hidden"], a["topk"], a["cap"], a["out"], None)
+    assert call(scale=float("nan")) == M.MOE_ERR_UNSUPPORTED
+    assert call(scale=float("inf")) == M.MOE_ERR_UNSUPPORTED
     assert call(hidden=100) == M.MOE_ERR_SHAPE
     assert call(topk=40) == M.MOE_ERR_SHAPE
     assert call(s2d=None) == M.MOE_ERR_NULL
