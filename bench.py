@@ -341,8 +341,10 @@ def main():
     R, T, nv, E = wl.rows, wl.topk, inp["num_valid"], wl.experts
     sH, sI = (H // 128) * sb, (I // 128) * sb
     row_in = 2 * H if std else H + sH   # a received row: bf16, or fp8 + scales
+    ids_v = inp["data"]["ids"][:nv]
+    r_live = int(((ids_v >= 0) & (ids_v < E)).any(axis=1).sum())   # rows read by the scatter
     st_bytes = {
-        "expand_layout": nv * T * 8 + A * row_in + m_used * (H + sH + 4) + R * T * 4
+        "expand_layout": nv * T * 8 + r_live * row_in + m_used * (H + sH + 4) + R * T * 4
                          + mod.capacity * 4,
         "gemm_gate_up": g1_bytes,
         "act_quant": A * 4 * I + m_used * (I + sI),

@@ -129,16 +129,29 @@ __global__ __launch_bounds__(kCountThreads) void expand_count_kernel(
   }
   if (bad) atomicOr(&lflag, MOE_FLAG_EXPERT_ID_RANGE);
   __syncthreads();
-  // Per expert (one wave each, lane = group, G <= 64 lanes): each group's
-  // exclusive offset within the block (group order preserved), and the
-  // block total.
+  // Each group's exclusive offset within the block per expert (group order
+  // preserved), and the block total.  Few experts: one wave per expert, lane
+  // = group (G <= 64).  Many: one thread per expert walks the G groups in
+  // order (a wave per expert would run E / 4 scans one after another).
   const int lane = t & 63, wid = t >> 6;
   const int64_t g0 = (int64_t)blockIdx.x * G;
-  for (int e = wid; e < E; e += kCountThreads / 64) {
-    const int c = lane < G ? cnt[lane * E + e] : 0;
-    const int incl = wave_incl_scan_i(c);
-    if (lane < G && g0 + lane < ngroups) grp[(g0 + lane) * E + e] = incl - c;
-    if (lane == 63) blk[(int64_t)blockIdx.x * E + e] = incl;
+  if (E <= 32) {
+    for (int e = wid; e < E; e += kCountThreads / 64) {
+      const int c = lane < G ? cnt[lane * E + e] : 0;
+      const int incl = wave_incl_scan_i(c);
+      if (lane < G && g0 + lane < ngroups) grp[(g0 + lane) * E + e] = incl - c;
+      if (lane == 63) blk[(int64_t)blockIdx.x * E + e] = incl;
+    }
+  } else {
+    for (int e = t; e < E; e += kCountThreads) {
+      int run = 0;
+      for (int g = 0; g < G; ++g) {
+        const int c = cnt[g * E + e];
+        if (g0 + g < ngroups) grp[(g0 + g) * E + e] = run;
+        run += c;
+      }
+      blk[(int64_t)blockIdx.x * E + e] = run;
+    }
   }
   if (t == 0) blk_flag[blockIdx.x] = lflag;
 }
@@ -357,9 +370,9 @@ __device__ __forceinline__ void quant_pass(const u32x4 (&v)[8], int c0, int nch,
   }
 }
 
-// kQ: bf16 input rows quantised here (x_scale unused); otherwise fp8 rows
-// and their scales are copied.
-template <bool kQ>
+// kQ: bf16 input rows quantised here (x_scale unused), with UE8M0 scales
+// when kQU8 (else fp32); otherwise fp8 rows and their scales are copied.
+template <bool kQ, bool kQU8>
 __global__ __launch_bounds__(kScatterThreads) void expand_scatter_kernel(
     const uint8_t* __restrict__ x, int64_t x_stride, const uint8_t* __restrict__ x_scale,
     int64_t x_scale_stride_bytes, int scale_bytes, const int32_t* __restrict__ ids,
@@ -409,7 +422,7 @@ __global__ __launch_bounds__(kScatterThreads) void expand_scatter_kernel(
     if (t == 0) l_flag = 0;
     __syncthreads();
     if (fl) atomicOr(&l_flag, fl);
-    if (nblk <= 8) {  // a thread per expert walks its few blocks
+    if (nblk <= 8 || E >= 64) {  // a thread per expert walks the blocks in order
       for (int e = t; e < E; e += kScatterThreads) {
         int run = 0;
         for (int b = 0; b < nblk; ++b) {
@@ -540,8 +553,7 @@ __global__ __launch_bounds__(kScatterThreads) void expand_scatter_kernel(
         // c / 16 (K-block-major) from the group's first lane.
         uint2 q[8];
         uint32_t sc[8];
-        if (scale_bytes == 1) quant_pass<true>(f.v, c0, nch_in, lane, q, sc);
-        else quant_pass<false>(f.v, c0, nch_in, lane, q, sc);
+        quant_pass<kQU8>(f.v, c0, nch_in, lane, q, sc);
         for (uint64_t mm = mask; mm; mm &= mm - 1) {
           const int dk = __shfl(d, __builtin_ctzll(mm), 64);
           uint2* dst = reinterpret_cast<uint2*>(ex + (int64_t)dk * hidden);
@@ -552,8 +564,8 @@ __global__ __launch_bounds__(kScatterThreads) void expand_scatter_kernel(
               dst[c] = q[u];
               if ((lane & 15) == 0) {
                 const int64_t at = (int64_t)(c >> 4) * capacity + dk;
-                if (scale_bytes == 4) reinterpret_cast<uint32_t*>(ex_scale)[at] = sc[u];
-                else ex_scale[at] = (uint8_t)sc[u];
+                if (kQU8) ex_scale[at] = (uint8_t)sc[u];
+                else reinterpret_cast<uint32_t*>(ex_scale)[at] = sc[u];
               }
             }
           }
@@ -692,7 +704,10 @@ moe_status expand_layout(bool bf16, const void* x, int64_t x_stride, const void*
   if (grid < 1024) grid = 1024;
   if (grid > 16384) grid = 16384;
   const size_t lds = (size_t(4) * E + 1 + (fold ? size_t(nb) * E : 0)) * 4;
-  hipLaunchKernelGGL(bf16 ? expand_scatter_kernel<true> : expand_scatter_kernel<false>,
+  auto scatter = !bf16 ? expand_scatter_kernel<false, false>
+                 : fmt == MOE_SCALE_UE8M0 ? expand_scatter_kernel<true, true>
+                                          : expand_scatter_kernel<true, false>;
+  hipLaunchKernelGGL(scatter,
                      dim3((unsigned)grid), dim3(kScatterThreads), lds, s,
                      (const uint8_t*)x, x_stride, (const uint8_t*)x_scale,
                      x_scale_stride * scale_bytes, scale_bytes, topk_ids, topk_weights,
