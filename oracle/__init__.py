@@ -20,6 +20,8 @@ It is a plain, slow, obviously-correct restatement of what the pages define:
              layer, the standard (non-EP) path (bf16 rows quantised per
              1x128 group, top-k weights and the routed scaling factor in the
              gather), and a per-token brute force that uses no layout at all.
+* ``masked`` the decode path's fixed-height masked slab: the bridges from
+             and back to the expanded layout and the layer on the slab.
 
 Sources (cited by title and section in every function):
 
@@ -38,4 +40,4 @@ quantisation at rounding ties after a different fp32 accumulation order are
 bounded only by the output tolerance (see the layer tests).
 """
 
-from . import fp8, quant, layout, layer  # noqa: F401
+from . import fp8, quant, layout, layer, masked  # noqa: F401

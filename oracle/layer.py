@@ -236,7 +236,11 @@ def brute_force(inp, mode: str = "auto", rows=None):
     Standard-path inputs (x_bf16 instead of x_q / x_s): each row is
     quantised per 1x128 group first, the weights are applied to the down
     output, and the sum is multiplied by routed_scaling_factor (default 1)
-    before the rounding."""
+    before the rounding.
+
+    mode 'masked' (the decode path's masked slab): each slot's down row is
+    weighted and rounded to bf16 before the sum, as the slab's bridge back
+    to the expanded layout does."""
     fmt = inp["fmt"]
     std = "x_bf16" in inp
     if mode == "auto":
@@ -289,6 +293,8 @@ def brute_force(inp, mode: str = "auto", rows=None):
             d = fp8.round_bf16(yq @ w2_of(e).T)[0]
             if mode == "post":
                 d = (d * wts[r, k]).astype(np.float32)
+            elif mode == "masked":
+                d = fp8.round_bf16((d * wts[r, k]).astype(np.float32))
             acc = (acc + d).astype(np.float32)
         out[i] = fp8.round_bf16((acc * rscale).astype(np.float32))
     return out
