@@ -220,7 +220,11 @@ def main():
         return
     inp = make_inputs(wl, dev)
     std = wl.input == "bf16"
-    if std:
+    masked = wl.max_m > 0
+    if masked:
+        mod = M.MaskedMoE(wl.rows, wl.topk, inp["w13"], inp["w13_scale"], inp["w2"],
+                          inp["w2_scale"], wl.align, wl.max_m, wl.fmt, device=dev)
+    elif std:
         mod = M.StandardMoE(wl.rows, wl.topk, inp["w13"], inp["w13_scale"], inp["w2"],
                             inp["w2_scale"], wl.align, wl.fmt, wl.routed_scale, device=dev)
     else:
@@ -229,35 +233,64 @@ def main():
     out = torch.empty((wl.rows, wl.hidden), dtype=torch.bfloat16, device=dev)
     fold = mod.row_weight if wl.fmt == "f32" and not std else None
 
-    def stage(i):
-        if i == 0:
-            if std:
-                mod.layout(inp["x"], inp["ids"], inp["w"])
-            else:
-                mod.layout(inp["x"], inp["x_scale"], inp["ids"], inp["w"], inp["prank"])
-        elif i == 1:
-            M.moe_grouped_gemm_fp8(mod.ex, mod.ex_scale, wl.fmt, mod.w13, mod.w13_scale,
-                                   mod.psum, mod.status, wl.align, mod.gate_up)
-        elif i == 2:
-            M.moe_act_quant(mod.gate_up, mod.m_indices, mod.psum, mod.status, mod.E, wl.align,
-                            wl.fmt, fold, mod.dq, mod.ds)
-        elif i == 3:
-            M.moe_grouped_gemm_fp8(mod.dq, mod.ds, wl.fmt, mod.w2, mod.w2_scale, mod.psum,
-                                   mod.status, wl.align, mod.down)
+    def layout_stage():
+        if std:
+            mod.layout(inp["x"], inp["ids"], inp["w"])
         else:
-            mod.gather(inp["w"], inp["prank"], out)
+            mod.layout(inp["x"], inp["x_scale"], inp["ids"], inp["w"], inp["prank"])
+
+    if masked:   # decode path: bridges into and out of the masked slab
+        mm = wl.max_m
+        stage_list = [
+            ("expand_layout", layout_stage),
+            ("to_slab", lambda: M.moe_expand_to_masked_slab(
+                mod.ex, mod.ex_scale, wl.fmt, mod.psum, mod.status, mod.E, wl.align, mm,
+                mod.slab, mod.slab_scale, mod.masked_m)),
+            ("gemm_gate_up", lambda: M.moe_grouped_gemm_fp8_masked(
+                mod.slab, mod.slab_scale, wl.fmt, mod.w13, mod.w13_scale, mod.masked_m, mm,
+                mod.s_gate_up)),
+            ("act_quant", lambda: M.moe_act_quant_masked(
+                mod.s_gate_up, mod.masked_m, mm, mod.E, wl.fmt, mod.s_dq, mod.s_ds)),
+            ("gemm_down", lambda: M.moe_grouped_gemm_fp8_masked(
+                mod.s_dq, mod.s_ds, wl.fmt, mod.w2, mod.w2_scale, mod.masked_m, mm,
+                mod.s_down)),
+            ("from_slab", lambda: M.moe_masked_slab_to_expand(
+                mod.s_down, mod.masked_m, mm, mod.psum, mod.status, mod.m_indices,
+                mod.row_weight, mod.E, wl.align, mod.down)),
+            ("gather", lambda: mod.gather(inp["w"], inp["prank"], out)),
+        ]
+    else:
+        stage_list = [
+            ("expand_layout", layout_stage),
+            ("gemm_gate_up", lambda: M.moe_grouped_gemm_fp8(
+                mod.ex, mod.ex_scale, wl.fmt, mod.w13, mod.w13_scale, mod.psum, mod.status,
+                wl.align, mod.gate_up)),
+            ("act_quant", lambda: M.moe_act_quant(
+                mod.gate_up, mod.m_indices, mod.psum, mod.status, mod.E, wl.align, wl.fmt,
+                fold, mod.dq, mod.ds)),
+            ("gemm_down", lambda: M.moe_grouped_gemm_fp8(
+                mod.dq, mod.ds, wl.fmt, mod.w2, mod.w2_scale, mod.psum, mod.status, wl.align,
+                mod.down)),
+            ("gather", lambda: mod.gather(inp["w"], inp["prank"], out)),
+        ]
+    names = [n for n, _ in stage_list]
+    NS = len(stage_list)
+    i_g1, i_g2 = names.index("gemm_gate_up"), names.index("gemm_down")
+
+    def stage(i):
+        stage_list[i][1]()
 
     if args.pmc_target == "gemm":     # layout once, then 3 x (gate_up, act, down)
         stage(0)
         for _ in range(3):
-            for i in (1, 2, 3):
+            for i in range(1, NS - 1):
                 stage(i)
         torch.cuda.synchronize()
         print(json.dumps({"pmc_target": "gemm", "status": mod.status.cpu().tolist()}))
         return
 
     for _ in range(args.warmup):
-        for i in range(5):
+        for i in range(NS):
             stage(i)
     torch.cuda.synchronize()
 
@@ -269,7 +302,7 @@ def main():
     torch.cuda.synchronize()
     t_start.record()
     for s in range(args.steps):
-        for i in range(5):
+        for i in range(NS):
             stage(i)
     t_end.record()
     torch.cuda.synchronize()
@@ -280,28 +313,28 @@ def main():
     # around its two launches (gate_up, down) on the stream they run on.
     ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
     for s in range(args.steps):
-        stage(0)
-        ev[s][0].record()
-        stage(1)
-        ev[s][1].record()
-        stage(2)
-        ev[s][2].record()
-        stage(3)
-        ev[s][3].record()
-        stage(4)
+        for i in range(NS):
+            if i == i_g1:
+                ev[s][0].record()
+            elif i == i_g2:
+                ev[s][2].record()
+            stage(i)
+            if i == i_g1:
+                ev[s][1].record()
+            elif i == i_g2:
+                ev[s][3].record()
     torch.cuda.synchronize()
     gemm1_us = float(np.mean([e[0].elapsed_time(e[1]) for e in ev])) * 1e3
     gemm2_us = float(np.mean([e[2].elapsed_time(e[3]) for e in ev])) * 1e3
 
     # Per-stage breakdown (after the timed region; events between stages).
-    sev = [[torch.cuda.Event(enable_timing=True) for _ in range(6)] for _ in range(10)]
+    sev = [[torch.cuda.Event(enable_timing=True) for _ in range(NS + 1)] for _ in range(10)]
     for s in range(10):
         sev[s][0].record()
-        for i in range(5):
+        for i in range(NS):
             stage(i)
             sev[s][i + 1].record()
     torch.cuda.synchronize()
-    names = ["expand_layout", "gemm_gate_up", "act_quant", "gemm_down", "gather"]
     stages_us = {n: float(np.median([sev[s][i].elapsed_time(sev[s][i + 1]) for s in range(10)]))
                  * 1e3 for i, n in enumerate(names)}
 
@@ -327,7 +360,8 @@ def main():
                 "unit": "TFLOP/s"}
     roof["frac"] = roof["achieved"] / roof["peak"]
     roof["traffic"] = measured_traffic(wl.name)
-    roof["kernel"] = (f"grouped_gemm_kernel<{str(wl.fmt == 'ue8m0').lower()}> "
+    roof["kernel"] = (f"grouped_gemm_kernel<{str(wl.fmt == 'ue8m0').lower()}, "
+                      f"{str(masked).lower()}> "
                       "(mean over its gate_up and down launches)")
     roof["launch_us"] = {"gate_up": gemm1_us, "down": gemm2_us, "mean": (gemm1_us + gemm2_us) / 2}
     roof["algorithmic_bytes_per_launch"] = byts / 2
@@ -347,9 +381,13 @@ def main():
         "expand_layout": nv * T * 8 + r_live * row_in + m_used * (H + sH + 4) + R * T * 4
                          + mod.capacity * 4,
         "gemm_gate_up": g1_bytes,
-        "act_quant": A * 4 * I + m_used * (I + sI),
+        "act_quant": A * 4 * I + (A if masked else m_used) * (I + sI),
         "gemm_down": g2_bytes,
         "gather": A * 2 * H + nv * 2 * H + nv * T * 8,
+        # bridges of the masked slab: live rows + scales copied in; down rows
+        # read, weighted, written back over every expanded row (pads zeroed)
+        "to_slab": 2 * A * (H + sH),
+        "from_slab": A * (2 * H + 4) + m_used * 2 * H,
     }
     st_flops = {"gemm_gate_up": g1_flops, "gemm_down": g2_flops}
     stages = {}
@@ -364,7 +402,7 @@ def main():
         stages[n] = rec
 
     cpu = None
-    if not args.no_cpu_baseline and not std:
+    if not args.no_cpu_baseline and not std and not masked:
         cpu = cpu_baseline(inp, wl, args.cpu_runs)
 
     res = {
@@ -381,6 +419,7 @@ def main():
         "dtype": "fp8_e4m3 (fp32 accumulate, bf16 out)",
         "data": "synthetic (seeded; routing/weights per the workload recipe)",
         "config": {"workload": wl.name, "input": wl.input, "routed_scaling_factor": wl.routed_scale,
+                   "masked_slab_max_m": wl.max_m,
                    "rows": wl.rows, "valid_rows": inp["num_valid"],
                    "hidden": H, "inter": I, "experts_local": wl.experts,
                    "experts_global": wl.global_experts, "topk": wl.topk,

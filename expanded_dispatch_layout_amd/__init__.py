@@ -8,13 +8,15 @@ binding raises if the library is missing: there is no fallback.
 Functions mirror the C ABI in ``include/moe_expand.h``:
 
     moe_expand_layout, moe_expand_layout_bf16, moe_grouped_gemm_fp8,
-    moe_act_quant, moe_gather, moe_expand_capacity, moe_expand_workspace_bytes,
-    moe_status_string
+    moe_act_quant, moe_gather, moe_expand_to_masked_slab,
+    moe_grouped_gemm_fp8_masked, moe_act_quant_masked, moe_masked_slab_to_expand,
+    moe_expand_capacity, moe_expand_workspace_bytes, moe_status_string
 
 plus :class:`ExpandedMoE`, which allocates the buffers once for a given
 receive-buffer size and runs the five calls of a layer in order, and
 :class:`StandardMoE`, the same for the standard (non-EP) path: bf16 token
-rows in, top-k weights and the routed scaling factor applied in the gather.
+rows in, top-k weights and the routed scaling factor applied in the gather,
+and :class:`MaskedMoE`, the decode path on a fixed-height masked slab.
 """
 
 import ctypes
@@ -28,7 +30,7 @@ HEADER_PATH = os.path.join(os.path.dirname(_HERE), "include", "moe_expand.h")
 MOE_OK, MOE_ERR_NULL, MOE_ERR_SHAPE, MOE_ERR_ALIGNMENT = 0, 1, 2, 3
 MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE, MOE_ERR_LAUNCH = 4, 5, 6
 MOE_SCALE_F32, MOE_SCALE_UE8M0 = 0, 1
-MOE_FLAG_CAPACITY_OVERFLOW, MOE_FLAG_EXPERT_ID_RANGE = 1, 2
+MOE_FLAG_CAPACITY_OVERFLOW, MOE_FLAG_EXPERT_ID_RANGE, MOE_FLAG_SLAB_OVERFLOW = 1, 2, 4
 FMT = {"f32": MOE_SCALE_F32, "ue8m0": MOE_SCALE_UE8M0}
 
 _P = ctypes.c_void_p
@@ -48,6 +50,11 @@ _SIGNATURES = {
                                   _P, _P]),
     "moe_act_quant": (_I, [_P, _P, _P, _P, _I64, _I, _I, _I, _I, _P, _P, _P, _P]),
     "moe_gather": (_I, [_P, _P, _P, ctypes.c_float, _P, _I, _I64, _I, _I, _I64, _P, _P]),
+    "moe_expand_to_masked_slab": (_I, [_P, _P, _I, _P, _P, _I64, _I, _I, _I, _I, _P, _P, _P,
+                                       _P]),
+    "moe_grouped_gemm_fp8_masked": (_I, [_P, _P, _I, _P, _P, _P, _I, _I, _I, _I, _P, _P]),
+    "moe_act_quant_masked": (_I, [_P, _P, _I, _I, _I, _I, _P, _P, _P]),
+    "moe_masked_slab_to_expand": (_I, [_P, _P, _I, _P, _P, _P, _P, _I64, _I, _I, _I, _P, _P]),
 }
 
 _lib = None
@@ -186,6 +193,47 @@ def moe_gather(expert_out, src2dst, topk_weights, psum_recv_per_rank, out, strea
     _check("moe_gather", code)
 
 
+def moe_expand_to_masked_slab(ex, ex_scale, fmt, psum, status, num_experts, align, max_m,
+                              slab, slab_scale, masked_m, stream=None):
+    """ex [capacity, H] fp8, ex_scale [H/128, capacity] -> slab [E*max_m, H],
+    slab_scale [H/128, E*max_m], masked_m [E]."""
+    capacity, hidden = ex.shape
+    code = lib().moe_expand_to_masked_slab(
+        _ptr(ex), _ptr(ex_scale), _fmt(fmt), _ptr(psum), _ptr(status), capacity, hidden,
+        num_experts, align, max_m, _ptr(slab), _ptr(slab_scale), _ptr(masked_m),
+        _stream(stream))
+    _check("moe_expand_to_masked_slab", code)
+
+
+def moe_grouped_gemm_fp8_masked(a, a_scale, fmt, w, w_scale, masked_m, max_m, out,
+                                stream=None):
+    """a [E*max_m, k] fp8, a_scale [k/128, E*max_m], w [E, n, k] -> out [E*max_m, n]."""
+    E, n, k = w.shape
+    code = lib().moe_grouped_gemm_fp8_masked(
+        _ptr(a), _ptr(a_scale), _fmt(fmt), _ptr(w), _ptr(w_scale), _ptr(masked_m), max_m,
+        n, k, E, _ptr(out), _stream(stream))
+    _check("moe_grouped_gemm_fp8_masked", code)
+
+
+def moe_act_quant_masked(gate_up, masked_m, max_m, num_experts, fmt, out, out_scale,
+                         stream=None):
+    """gate_up [E*max_m, 2I] bf16 -> out [E*max_m, I] fp8, out_scale [I/128, E*max_m]."""
+    code = lib().moe_act_quant_masked(
+        _ptr(gate_up), _ptr(masked_m), max_m, gate_up.shape[1] // 2, num_experts, _fmt(fmt),
+        _ptr(out), _ptr(out_scale), _stream(stream))
+    _check("moe_act_quant_masked", code)
+
+
+def moe_masked_slab_to_expand(slab_out, masked_m, max_m, psum, status, m_indices, row_weight,
+                              num_experts, align, out, stream=None):
+    """slab_out [E*max_m, H] bf16 -> out [capacity, H] bf16 (weighted rows)."""
+    capacity, hidden = out.shape
+    code = lib().moe_masked_slab_to_expand(
+        _ptr(slab_out), _ptr(masked_m), max_m, _ptr(psum), _ptr(status), _ptr(m_indices),
+        _ptr(row_weight), capacity, hidden, num_experts, align, _ptr(out), _stream(stream))
+    _check("moe_masked_slab_to_expand", code)
+
+
 class ExpandedMoE:
     """Buffers for one receive-buffer size, and the layer's five calls.
 
@@ -292,3 +340,44 @@ class StandardMoE(ExpandedMoE):
         self.experts(stream)
         self.gather(topk_weights, psum_recv_per_rank, out, stream)
         return out
+
+
+class MaskedMoE(ExpandedMoE):
+    """The decode path: the expanded layout, then the bridge into a
+    fixed-height slab [E, max_m, H] with masked_m live rows per expert, the
+    masked GEMMs and activation on the slab, the bridge back with the top-k
+    weights, and the combine with weight 1."""
+
+    def __init__(self, rows, topk, w13, w13_scale, w2, w2_scale, align, max_m, fmt="f32",
+                 device="cuda"):
+        import torch
+        super().__init__(rows, topk, w13, w13_scale, w2, w2_scale, align, fmt, device)
+        self.max_m = max_m
+        E, H, I = self.E, self.H, self.I
+        sdt = torch.float32 if fmt == "f32" else torch.uint8
+        n = E * max_m
+        self.slab = torch.empty((n, H), dtype=torch.uint8, device=device)
+        self.slab_scale = torch.empty((H // 128, n), dtype=sdt, device=device)
+        self.masked_m = torch.empty(E, dtype=torch.int32, device=device)
+        self.s_gate_up = torch.empty((n, 2 * I), dtype=torch.bfloat16, device=device)
+        self.s_dq = torch.empty((n, I), dtype=torch.uint8, device=device)
+        self.s_ds = torch.empty((I // 128, n), dtype=sdt, device=device)
+        self.s_down = torch.empty((n, H), dtype=torch.bfloat16, device=device)
+
+    def experts(self, stream=None):
+        moe_expand_to_masked_slab(self.ex, self.ex_scale, self.fmt, self.psum, self.status,
+                                  self.E, self.align, self.max_m, self.slab, self.slab_scale,
+                                  self.masked_m, stream)
+        moe_grouped_gemm_fp8_masked(self.slab, self.slab_scale, self.fmt, self.w13,
+                                    self.w13_scale, self.masked_m, self.max_m, self.s_gate_up,
+                                    stream)
+        moe_act_quant_masked(self.s_gate_up, self.masked_m, self.max_m, self.E, self.fmt,
+                             self.s_dq, self.s_ds, stream)
+        moe_grouped_gemm_fp8_masked(self.s_dq, self.s_ds, self.fmt, self.w2, self.w2_scale,
+                                    self.masked_m, self.max_m, self.s_down, stream)
+        moe_masked_slab_to_expand(self.s_down, self.masked_m, self.max_m, self.psum,
+                                  self.status, self.m_indices, self.row_weight, self.E,
+                                  self.align, self.down, stream)
+
+    def gather(self, topk_weights, psum_recv_per_rank, out, stream=None):
+        moe_gather(self.down, self.src2dst, None, psum_recv_per_rank, out, stream)

@@ -11,7 +11,7 @@ INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(HERE, "libmoe_expand.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
-SOURCES = ["abi.cpp", "layout.hip", "gemm.hip", "act_quant.hip", "gather.hip"]
+SOURCES = ["abi.cpp", "layout.hip", "gemm.hip", "act_quant.hip", "gather.hip", "masked.hip"]
 
 FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared",

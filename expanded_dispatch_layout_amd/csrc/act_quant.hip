@@ -26,26 +26,36 @@ __device__ __forceinline__ float silu_mul(float g, float u) {
   return __fmul_rn(__fdiv_rn(g, den), u);
 }
 
-template <bool kUe8m0, bool kFold>
+// kMasked (the decode path's slab, rows e * max_m + i): `m_indices` is
+// masked_m, `psum` and `status` are unused, capacity = E * max_m; rows with
+// i >= masked_m[e] are neither read nor written (nothing reads them).
+template <bool kUe8m0, bool kFold, bool kMasked>
 __global__ __launch_bounds__(kThreads) void act_quant_kernel(
     const uint16_t* __restrict__ gu, const int32_t* __restrict__ m_indices,
     const int32_t* __restrict__ psum, const int32_t* __restrict__ status, int64_t capacity,
-    int inter, int E, const float* __restrict__ fold_w, uint8_t* __restrict__ out,
+    int inter, int E, int max_m, const float* __restrict__ fold_w, uint8_t* __restrict__ out,
     uint8_t* __restrict__ out_scale) {
   const int t = threadIdx.x, lane = t & 63;
   const int ngroups = inter / kGroup;
   // Round trip 1: the total and this workgroup's first label together (the
   // grid never exceeds the capacity, so row blockIdx.x is in bounds).
   int64_t m = blockIdx.x;
-  int e_next = m_indices[m];
-  const int64_t nrows = min((int64_t)status[0], capacity);
+  int e_next = kMasked ? 0 : m_indices[m];
+  const int64_t nrows = kMasked ? capacity : min((int64_t)status[0], capacity);
   for (; m < nrows; m += gridDim.x) {
-    const int e = e_next;
-    if (m + gridDim.x < nrows) e_next = m_indices[m + gridDim.x];
-    if (e < 0 || e >= E) continue;  // uniform per workgroup
+    int e, pe;
+    if constexpr (kMasked) {
+      e = (int)(m / max_m);
+      pe = e * max_m + max(0, min(m_indices[e], max_m));
+      if (m >= pe) continue;  // past the slab's live rows
+    } else {
+      e = e_next;
+      if (m + gridDim.x < nrows) e_next = m_indices[m + gridDim.x];
+      if (e < 0 || e >= E) continue;  // uniform per workgroup
+    }
     // Round trip 2: the expert's end, the fold weight and the row's first
     // pass, loaded together; a pad row's (unwritten) G values are never used.
-    const int pe = psum[e];
+    if constexpr (!kMasked) pe = psum[e];
     const float w = kFold ? fold_w[m] : 1.f;
     const uint16_t* grow = gu + m * (int64_t)(2 * inter);
     u32x4 gv0 = {0u, 0u, 0u, 0u}, uv0 = {0u, 0u, 0u, 0u};
@@ -139,11 +149,36 @@ extern "C" moe_status moe_act_quant(const void* gate_up, const int32_t* m_indice
   if (capacity == 0) return MOE_OK;
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   int64_t grid = capacity < 2048 ? capacity : 2048;  // grid-stride over the live rows
-  auto kern = fmt == MOE_SCALE_UE8M0 ? act_quant_kernel<true, false>
-              : fold_weight           ? act_quant_kernel<false, true>
-                                      : act_quant_kernel<false, false>;
+  auto kern = fmt == MOE_SCALE_UE8M0 ? act_quant_kernel<true, false, false>
+              : fold_weight           ? act_quant_kernel<false, true, false>
+                                      : act_quant_kernel<false, false, false>;
   hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(kThreads), 0, s, (const uint16_t*)gate_up,
-                     m_indices, psum, status, capacity, inter, num_experts, fold_weight,
+                     m_indices, psum, status, capacity, inter, num_experts, 0, fold_weight,
+                     (uint8_t*)out, (uint8_t*)out_scale);
+  if (hipGetLastError() != hipSuccess) return MOE_ERR_LAUNCH;
+  return MOE_OK;
+}
+
+extern "C" moe_status moe_act_quant_masked(const void* gate_up, const int32_t* masked_m,
+                                           int max_m, int inter, int num_experts,
+                                           moe_scale_fmt fmt, void* out, void* out_scale,
+                                           void* stream) {
+  if (max_m < 0 || max_m > (1 << 24) || max_m % 16 || inter <= 0 || inter % kGroup != 0 ||
+      num_experts < 1 || num_experts > MOE_MAX_EXPERTS ||
+      (int64_t)max_m * num_experts > (1LL << 30))
+    return MOE_ERR_SHAPE;
+  if (fmt != MOE_SCALE_F32 && fmt != MOE_SCALE_UE8M0) return MOE_ERR_UNSUPPORTED;
+  if (!masked_m) return MOE_ERR_NULL;
+  if (max_m > 0 && (!gate_up || !out || !out_scale)) return MOE_ERR_NULL;
+  if (((uintptr_t)gate_up % 16) || ((uintptr_t)out % 16)) return MOE_ERR_ALIGNMENT;
+  const int64_t rows = (int64_t)max_m * num_experts;
+  if (rows == 0) return MOE_OK;
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  const int64_t grid = rows < 2048 ? rows : 2048;  // grid-stride over the slab rows
+  auto kern = fmt == MOE_SCALE_UE8M0 ? act_quant_kernel<true, false, true>
+                                     : act_quant_kernel<false, false, true>;
+  hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(kThreads), 0, s, (const uint16_t*)gate_up,
+                     masked_m, nullptr, nullptr, rows, inter, num_experts, max_m, nullptr,
                      (uint8_t*)out, (uint8_t*)out_scale);
   if (hipGetLastError() != hipSuccess) return MOE_ERR_LAUNCH;
   return MOE_OK;

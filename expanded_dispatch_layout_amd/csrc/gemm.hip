@@ -46,6 +46,10 @@
 //    matrix core accumulates the scaled products directly.
 //  - The bf16 output tile is staged through LDS and written with 16-byte
 //    stores; rows past the group are never written.
+//  - Masked mode (the decode path's fixed-height slab, SGLang
+//    moe_runner/deep_gemm.py source, _run_masked_gemm; SGLang PR 37261, "Why
+//    decode stays on V1 low_latency"): expert e owns slab rows
+//    [e * max_m, e * max_m + masked_m[e]); only the item decode differs.
 #include "common.hpp"
 
 namespace moe {
@@ -556,7 +560,9 @@ __device__ __forceinline__ void kloop_role(int role, uint32_t lds0, v4f (&acc)[F
   }
 }
 
-template <bool kUe8m0>
+// kMasked: `psum` is masked_m, `align` is max_m, `status` is unused and the
+// activation rows are the E * max_m slab rows (capacity).
+template <bool kUe8m0, bool kMasked>
 __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(
     const uint8_t* __restrict__ a, const uint8_t* __restrict__ a_scale,
     const uint8_t* __restrict__ w, const uint8_t* __restrict__ w_scale,
@@ -564,13 +570,13 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(
     int K, int E, int align, uint16_t* __restrict__ out) {
   __shared__ __attribute__((aligned(16))) uint8_t lds[LDS_BYTES];
   __shared__ int gp[MOE_MAX_EXPERTS + 1];  // prefix of row groups per expert
-  __shared__ int pe[MOE_MAX_EXPERTS];      // psum, kept for the item decode
+  __shared__ int pe[MOE_MAX_EXPERTS];      // end of each expert's live rows
   const int t = threadIdx.x, lane = t & 63;
   const int wid = __builtin_amdgcn_readfirstlane(t >> 6);  // uniform per wave
   const int wm = wid / WAVES_N, wn = wid % WAVES_N;
   const FragOffsets fo = frag_offsets(lane, wm, wn);
   const uint32_t lds0 = lds_addr(lds);
-  const int64_t nrows = min((int64_t)status[0], capacity);
+  const int64_t nrows = kMasked ? capacity : min((int64_t)status[0], capacity);
   const int sbytes = kUe8m0 ? 1 : 4;
   const int KB = K / BK, NT = N / BN;
 
@@ -582,11 +588,18 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(
       const int e = e0 + lane;
       int ng = 0;
       if (e < E) {
-        const int p_e = psum[e];
-        const int64_t st = e ? align_up_i(psum[e - 1], align) : 0;
-        const int64_t en = min((int64_t)align_up_i(p_e, align), nrows);
-        ng = en > st ? (int)((en - st + GM - 1) / GM) : 0;
-        pe[e] = p_e;
+        if (kMasked) {  // slab: rows [e * max_m, + masked_m[e]), no padding
+          const int64_t st = (int64_t)e * align;
+          const int64_t en = st + max(0, min(psum[e], align));
+          ng = (int)((en - st + GM - 1) / GM);
+          pe[e] = (int)en;
+        } else {
+          const int p_e = psum[e];
+          const int64_t st = e ? align_up_i(psum[e - 1], align) : 0;
+          const int64_t en = min((int64_t)align_up_i(p_e, align), nrows);
+          ng = en > st ? (int)((en - st + GM - 1) / GM) : 0;
+          pe[e] = p_e;
+        }
       }
       const int incl = wave_incl_scan_i(ng);
       if (e < E) gp[e] = run + incl - ng;
@@ -615,7 +628,7 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(
     const int ge = gp[e + 1] - gp[e];  // row groups of expert e (>= 1 here)
     const int64_t local = item - (int64_t)NT * gp[e];
     const int nt = (int)(local / ge), gi = gp[e] + (int)(local % ge);
-    const int64_t st = e ? align_up_i(pe[e - 1], align) : 0;
+    const int64_t st = kMasked ? (int64_t)e * align : (e ? align_up_i(pe[e - 1], align) : 0);
     const int64_t m0 = st + (int64_t)(gi - gp[e]) * GM;
     const int64_t live = min((int64_t)GM, min((int64_t)pe[e], nrows) - m0);
     if (live <= 0) continue;  // only alignment padding: nothing to compute
@@ -693,6 +706,27 @@ int device_cus() {
   return cus[dev];
 }
 
+// One workgroup per CU (the kernel uses ~154 KB of LDS), a whole number per
+// XCD, never more than the largest possible number of work items.
+moe_status launch_gemm(bool masked, const void* a, const void* a_scale, moe_scale_fmt fmt,
+                       const void* w, const void* w_scale, const int32_t* psum,
+                       const int32_t* status, int64_t capacity, int n, int k, int num_experts,
+                       int align, void* out, void* stream) {
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  const int64_t max_items = ((capacity + GM - 1) / GM + num_experts) * (int64_t)(n / BN);
+  int64_t grid = device_cus();
+  if (grid > max_items) grid = max_items;
+  grid = (grid + kXcds - 1) / kXcds * kXcds;
+  auto kern = fmt == MOE_SCALE_UE8M0 ? (masked ? grouped_gemm_kernel<true, true>
+                                               : grouped_gemm_kernel<true, false>)
+                                     : (masked ? grouped_gemm_kernel<false, true>
+                                               : grouped_gemm_kernel<false, false>);
+  hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(kThreads), 0, s, (const uint8_t*)a,
+                     (const uint8_t*)a_scale, (const uint8_t*)w, (const uint8_t*)w_scale, psum,
+                     status, capacity, n, k, num_experts, align, (uint16_t*)out);
+  return hipGetLastError() == hipSuccess ? MOE_OK : MOE_ERR_LAUNCH;
+}
+
 }  // namespace
 }  // namespace moe
 
@@ -716,22 +750,31 @@ extern "C" moe_status moe_grouped_gemm_fp8(const void* a, const void* a_scale, m
       ((uintptr_t)a_scale % (fmt == MOE_SCALE_F32 ? 16 : 4)) || ((uintptr_t)w_scale % 4))
     return MOE_ERR_ALIGNMENT;
   if (capacity == 0) return MOE_OK;
-  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
-  // One workgroup per CU (the kernel uses ~154 KB of LDS), a whole number per
-  // XCD, never more than the largest possible number of work items.
-  const int64_t max_items = ((capacity + GM - 1) / GM + num_experts) * (int64_t)(n / BN);
-  int64_t grid = device_cus();
-  if (grid > max_items) grid = max_items;
-  grid = (grid + kXcds - 1) / kXcds * kXcds;
-  if (fmt == MOE_SCALE_UE8M0)
-    hipLaunchKernelGGL((grouped_gemm_kernel<true>), dim3((unsigned)grid), dim3(kThreads), 0, s,
-                       (const uint8_t*)a, (const uint8_t*)a_scale, (const uint8_t*)w,
-                       (const uint8_t*)w_scale, psum, status, capacity, n, k, num_experts, align,
-                       (uint16_t*)out);
-  else
-    hipLaunchKernelGGL((grouped_gemm_kernel<false>), dim3((unsigned)grid), dim3(kThreads), 0, s,
-                       (const uint8_t*)a, (const uint8_t*)a_scale, (const uint8_t*)w,
-                       (const uint8_t*)w_scale, psum, status, capacity, n, k, num_experts, align,
-                       (uint16_t*)out);
-  return hipGetLastError() == hipSuccess ? MOE_OK : MOE_ERR_LAUNCH;
+  return launch_gemm(false, a, a_scale, fmt, w, w_scale, psum, status, capacity, n, k,
+                     num_experts, align, out, stream);
+}
+
+extern "C" moe_status moe_grouped_gemm_fp8_masked(const void* a, const void* a_scale,
+                                                  moe_scale_fmt fmt, const void* w,
+                                                  const void* w_scale, const int32_t* masked_m,
+                                                  int max_m, int n, int k, int num_experts,
+                                                  void* out, void* stream) {
+  if (max_m < 0 || max_m > (1 << 24) || n <= 0 || k <= 0 || n % BN || k % BK ||
+      num_experts < 1 || num_experts > MOE_MAX_EXPERTS ||
+      (int64_t)max_m * num_experts > (1LL << 30))
+    return MOE_ERR_SHAPE;
+  if (fmt != MOE_SCALE_F32 && fmt != MOE_SCALE_UE8M0) return MOE_ERR_UNSUPPORTED;
+  if (!masked_m || !w || !w_scale) return MOE_ERR_NULL;
+  if (max_m > 0 && (!a || !a_scale || !out)) return MOE_ERR_NULL;
+  if (k / BK > MAX_KB) return MOE_ERR_UNSUPPORTED;
+  if (((uintptr_t)a % 16) || ((uintptr_t)w % 16) || ((uintptr_t)out % 16) ||
+      ((uintptr_t)a_scale % (fmt == MOE_SCALE_F32 ? 16 : 4)) || ((uintptr_t)w_scale % 4))
+    return MOE_ERR_ALIGNMENT;
+  // Every expert's slab starts on a 16-row boundary (the UE8M0 scale loads
+  // read aligned 4-byte words of a row group's scales).
+  if (max_m % 16) return MOE_ERR_SHAPE;
+  const int64_t rows = (int64_t)max_m * num_experts;
+  if (rows == 0) return MOE_OK;
+  return launch_gemm(true, a, a_scale, fmt, w, w_scale, masked_m, nullptr, rows, n, k,
+                     num_experts, max_m, out, stream);
 }

@@ -24,6 +24,18 @@
  * they are scattered) and leaving through moe_gather with the top-k weights
  * and the routed scaling factor.
  *
+ * The decode path's masked slab [P1 "Why decode stays on V1 low_latency";
+ * P3 pre_permute_deepep_v2_to_deep_gemm / post_permute_deep_gemm_to_
+ * deepep_v2, masked branches; _run_masked_gemm] runs after moe_expand_layout:
+ *   moe_expand_to_masked_slab    expanded rows -> fixed-height slab
+ *                                [num_experts, max_m, hidden], masked_m
+ *   moe_grouped_gemm_fp8_masked  gate_up on each expert's masked_m rows
+ *   moe_act_quant_masked         SiLU(gate)*up + per-1x128 quantisation
+ *   moe_grouped_gemm_fp8_masked  down
+ *   moe_masked_slab_to_expand    back to the expanded rows, times the top-k
+ *                                weights
+ *   moe_gather                   combine with weight 1
+ *
  * Sources, by page and section:
  *  [P1] SGLang pull request 37261, "feat(deepep_v2): expanded (do_expand=True)
  *       prefill dispatch for DeepEP-V2": Modifications/Core (row labels from
@@ -106,6 +118,9 @@ typedef enum {
                                         get -1)                               */
 #define MOE_FLAG_EXPERT_ID_RANGE 2   /* a valid row held an id >= num_experts;
                                         that slot was skipped                 */
+#define MOE_FLAG_SLAB_OVERFLOW 4     /* (moe_expand_to_masked_slab) an expert
+                                        had more than max_m live rows; rows
+                                        past max_m were dropped               */
 
 /* Limits of this build. */
 #define MOE_MAX_EXPERTS 1024
@@ -289,6 +304,71 @@ moe_status moe_gather(
     float routed_scaling_factor, const int32_t* psum_recv_per_rank, int num_src_ranks,
     int64_t rows, int hidden, int topk, int64_t capacity,
     void* out, void* stream);
+
+/*
+ * Expanded rows -> the decode path's masked slab [P1 "Why decode stays on V1
+ * low_latency": the fixed-height slab and the bridge into it; P3
+ * pre_permute_deepep_v2_to_deep_gemm, masked branch].
+ *
+ *   ex, ex_scale   as written by moe_expand_layout (scales [hidden/128,
+ *                  capacity] K-block-major), psum and status likewise
+ *   slab           [num_experts * max_m, hidden] fp8: row e * max_m + i =
+ *                  expanded row align(psum[e-1]) + i for i < masked_m[e]
+ *   slab_scale     [hidden/128, num_experts * max_m] K-block-major
+ *   masked_m       [num_experts] int32 = min(live rows of e, max_m)
+ * Slab rows past masked_m[e] are not written.  An expert with more than
+ * max_m live rows sets MOE_FLAG_SLAB_OVERFLOW in status[1] (written here:
+ * status is read-write) and its rows past max_m are dropped.
+ * Sizes: max_m >= 16 and a multiple of 16; num_experts * max_m <= 2^30.
+ */
+moe_status moe_expand_to_masked_slab(
+    const void* ex, const void* ex_scale, moe_scale_fmt fmt, const int32_t* psum,
+    int32_t* status, int64_t capacity, int hidden, int num_experts, int align, int max_m,
+    void* slab, void* slab_scale, int32_t* masked_m, void* stream);
+
+/*
+ * Masked grouped fp8 GEMM [P3 _run_masked_gemm]: as moe_grouped_gemm_fp8 on
+ * the slab, expert e's rows being [e * max_m, e * max_m + masked_m[e]).
+ *   a        [num_experts * max_m, k] fp8, a_scale [k/128, num_experts * max_m]
+ *   w, w_scale as moe_grouped_gemm_fp8
+ *   out      [num_experts * max_m, n] bf16; rows past masked_m[e] unwritten
+ * Sizes: max_m a multiple of 16; n, k multiples of 128.
+ */
+moe_status moe_grouped_gemm_fp8_masked(
+    const void* a, const void* a_scale, moe_scale_fmt fmt, const void* w,
+    const void* w_scale, const int32_t* masked_m, int max_m, int n, int k,
+    int num_experts, void* out, void* stream);
+
+/*
+ * SiLU(gate)*up and per-1x128 fp8 quantisation of the slab's live rows
+ * [P3 _run_masked_gemm's activation; the rule of moe_act_quant, no fold]:
+ *   gate_up  [num_experts * max_m, 2*inter] bf16
+ *   out      [num_experts * max_m, inter] fp8, out_scale [inter/128,
+ *            num_experts * max_m] K-block-major
+ * Rows past masked_m[e] are neither read nor written.
+ */
+moe_status moe_act_quant_masked(
+    const void* gate_up, const int32_t* masked_m, int max_m, int inter,
+    int num_experts, moe_scale_fmt fmt, void* out, void* out_scale, void* stream);
+
+/*
+ * The slab's down rows back to the expanded layout [P1 "Why decode stays on
+ * V1 low_latency"; P3 post_permute_deep_gemm_to_deepep_v2, masked branch:
+ * the top-k weights are applied here, the expanded combine takes none].
+ *   slab_out    [num_experts * max_m, hidden] bf16
+ *   masked_m, max_m  as written / used by moe_expand_to_masked_slab
+ *   psum, status, m_indices  from moe_expand_layout
+ *   row_weight  [capacity] fp32 top-k weight of each expanded row, or NULL
+ *   out         [capacity, hidden] bf16: for every expanded row m below the
+ *               total, of expert e at i = m - align(psum[e-1]):
+ *               bf16(row_weight[m] * slab_out[e * max_m + i]) if i <
+ *               masked_m[e] (fp32 product, one rounding; a copy when
+ *               row_weight is NULL), else 0.  Rows past the total untouched.
+ */
+moe_status moe_masked_slab_to_expand(
+    const void* slab_out, const int32_t* masked_m, int max_m, const int32_t* psum,
+    const int32_t* status, const int32_t* m_indices, const float* row_weight,
+    int64_t capacity, int hidden, int num_experts, int align, void* out, void* stream);
 
 #ifdef __cplusplus
 }

@@ -22,6 +22,8 @@ def test_library_exports_every_header_function():
     names = M.header_functions()
     assert set(names) >= {"moe_expand_layout", "moe_expand_layout_bf16",
                           "moe_grouped_gemm_fp8", "moe_act_quant",
+                          "moe_expand_to_masked_slab", "moe_grouped_gemm_fp8_masked",
+                          "moe_act_quant_masked", "moe_masked_slab_to_expand",
                           "moe_gather", "moe_expand_capacity",
                           "moe_expand_workspace_bytes", "moe_status_string"}
     lib = M.lib()
@@ -152,6 +154,61 @@ def test_layout_bf16_rejects_bad_arguments():
     assert _layout_bf16(rw=FAKE, w=None) == M.MOE_ERR_NULL
     assert _layout_bf16(ws=None) == M.MOE_ERR_WORKSPACE
     assert _layout_bf16(wsb=16) == M.MOE_ERR_WORKSPACE       # everything else valid
+
+
+def test_masked_entry_points_reject_bad_arguments():
+    L = M.lib()
+
+    def slab(**kw):
+        a = dict(ex=FAKE, exs=FAKE, fmt=0, psum=FAKE, st=FAKE, cap=320, hidden=256, E=4,
+                 align=64, max_m=64, slab=FAKE, ss=FAKE, mm=FAKE)
+        a.update(kw)
+        return L.moe_expand_to_masked_slab(a["ex"], a["exs"], a["fmt"], a["psum"], a["st"],
+                                           a["cap"], a["hidden"], a["E"], a["align"],
+                                           a["max_m"], a["slab"], a["ss"], a["mm"], None)
+    assert slab(max_m=8) == M.MOE_ERR_SHAPE
+    assert slab(max_m=40) == M.MOE_ERR_SHAPE
+    assert slab(hidden=100) == M.MOE_ERR_SHAPE
+    assert slab(align=48) == M.MOE_ERR_UNSUPPORTED
+    assert slab(fmt=5) == M.MOE_ERR_UNSUPPORTED
+    assert slab(mm=None) == M.MOE_ERR_NULL
+    assert slab(slab=MIS) == M.MOE_ERR_ALIGNMENT
+
+    def gemm(**kw):
+        a = dict(a=FAKE, as_=FAKE, fmt=0, w=FAKE, ws=FAKE, mm=FAKE, max_m=64, n=256, k=256,
+                 E=4, out=FAKE)
+        a.update(kw)
+        return L.moe_grouped_gemm_fp8_masked(a["a"], a["as_"], a["fmt"], a["w"], a["ws"],
+                                             a["mm"], a["max_m"], a["n"], a["k"], a["E"],
+                                             a["out"], None)
+    assert gemm(max_m=40) == M.MOE_ERR_SHAPE
+    assert gemm(n=100) == M.MOE_ERR_SHAPE
+    assert gemm(mm=None) == M.MOE_ERR_NULL
+    assert gemm(out=MIS) == M.MOE_ERR_ALIGNMENT
+    assert gemm(max_m=0) == M.MOE_OK                 # nothing to do, nothing launched
+
+    def act(**kw):
+        a = dict(gu=FAKE, mm=FAKE, max_m=64, inter=128, E=4, fmt=0, out=FAKE, os=FAKE)
+        a.update(kw)
+        return L.moe_act_quant_masked(a["gu"], a["mm"], a["max_m"], a["inter"], a["E"],
+                                      a["fmt"], a["out"], a["os"], None)
+    assert act(inter=100) == M.MOE_ERR_SHAPE
+    assert act(max_m=20) == M.MOE_ERR_SHAPE
+    assert act(mm=None) == M.MOE_ERR_NULL
+    assert act(gu=MIS) == M.MOE_ERR_ALIGNMENT
+    assert act(max_m=0) == M.MOE_OK
+
+    def back(**kw):
+        a = dict(so=FAKE, mm=FAKE, max_m=64, psum=FAKE, st=FAKE, mi=FAKE, rw=None, cap=320,
+                 hidden=256, E=4, align=64, out=FAKE)
+        a.update(kw)
+        return L.moe_masked_slab_to_expand(a["so"], a["mm"], a["max_m"], a["psum"], a["st"],
+                                           a["mi"], a["rw"], a["cap"], a["hidden"], a["E"],
+                                           a["align"], a["out"], None)
+    assert back(max_m=0) == M.MOE_ERR_SHAPE
+    assert back(mi=None) == M.MOE_ERR_NULL
+    assert back(out=MIS) == M.MOE_ERR_ALIGNMENT
+    assert back(cap=0) == M.MOE_OK
 
 
 def test_gather_rejects_bad_arguments():

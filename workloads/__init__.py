@@ -30,6 +30,11 @@ std_dsv3           standard single-GPU MoE of the DeepSeek-V3 shape: bf16
                    the GPU (11 GB of fp8 weights), top-8 uniform,
                    alignment 128, fp32 scales, routed scaling factor 2.5
                    (the model's own)
+dsv3_decode        decode share on the masked slab: 1024 received rows
+                   (32 tokens from each of 32 source ranks), H=7168,
+                   I=2048, 8 local of 256 experts, top-8 uniform,
+                   alignment 128, fp32 scales, slab height max_m=128
+                   (about four times the ~32 rows an expert expects)
 =================  =====================================================
 
 Recipe (numpy PCG64, seed 1000 + index): routing by Gumbel top-T over the
@@ -64,6 +69,7 @@ class Workload:
     seed: int = 1000
     input: str = "fp8"      # 'fp8' (received, quantised) or 'bf16' (standard path)
     routed_scale: float = 1.0   # routed scaling factor applied in the gather
+    max_m: int = 0          # >0: decode path on a masked slab of this height
     extra: dict = field(default_factory=dict)
 
 
@@ -85,6 +91,8 @@ WORKLOADS = {
                          input="bf16", routed_scale=2.5),
     "std_dsv3": Workload("std_dsv3", 4096, 7168, 2048, 256, 256, 8, 128,
                          seed=1007, input="bf16", routed_scale=2.5),
+    "dsv3_decode": Workload("dsv3_decode", 1024, 7168, 2048, 8, 256, 8, 128,
+                            seed=1008, max_m=128),
 }
 
 
