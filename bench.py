@@ -384,10 +384,10 @@ def main():
         "act_quant": A * 4 * I + (A if masked else m_used) * (I + sI),
         "gemm_down": g2_bytes,
         "gather": A * 2 * H + nv * 2 * H + nv * T * 8,
-        # bridges of the masked slab: live rows + scales copied in; down rows
-        # read, weighted, written back over every expanded row (pads zeroed)
+        # bridges of the masked slab: live rows + scales copied in; the live
+        # down rows and their weights read, weighted, written back
         "to_slab": 2 * A * (H + sH),
-        "from_slab": A * (2 * H + 4) + m_used * 2 * H,
+        "from_slab": A * (4 * H + 4),
     }
     st_flops = {"gemm_gate_up": g1_flops, "gemm_down": g2_flops}
     stages = {}

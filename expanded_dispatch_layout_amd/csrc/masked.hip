@@ -18,8 +18,10 @@
 //    whose live rows exceed max_m.
 //  - from_slab: expanded row m (below the device-side total) of expert e at
 //    i = m - align(psum[e-1]) <- bf16(w[m] * slab[e * max_m + i]) for
-//    i < masked_m[e] (fp32 product, one rounding; a copy without weights),
-//    zeros otherwise (alignment pads, dropped rows).
+//    i < masked_m[e] (fp32 product, one rounding; a copy without weights);
+//    rows the slab height dropped (masked_m[e] <= i < count_e) are zeroed,
+//    since their slots still point at them; alignment pad rows are left
+//    alone (no slot points at them, the combine never reads them).
 #include "common.hpp"
 
 namespace moe {
@@ -87,13 +89,15 @@ __global__ __launch_bounds__(kThreads) void from_slab_kernel(
        m += (int64_t)gridDim.x * kRowsPerBlock) {
     const int e = m_indices[m];
     u32x4* d = reinterpret_cast<u32x4*>(out + m * hidden);
-    int i = -1, n = 0;
+    int i = -1, n = 0, cnt = 0;
     if (e >= 0 && e < E) {
       const int st = e ? align_up_i(psum[e - 1], align) : 0;
       i = (int)(m - st);
       n = max(0, min(masked_m[e], max_m));
+      cnt = psum[e] - st;
     }
-    if (i < 0 || i >= n) {  // alignment pad or dropped row
+    if (i < 0 || i >= cnt) continue;  // alignment pad row: not read by anyone
+    if (i >= n) {                     // dropped by the slab height: zeros
       const u32x4 z = {0u, 0u, 0u, 0u};
       for (int c = lane; c < nch; c += 64) d[c] = z;
       continue;

@@ -363,7 +363,9 @@ moe_status moe_act_quant_masked(
  *               total, of expert e at i = m - align(psum[e-1]):
  *               bf16(row_weight[m] * slab_out[e * max_m + i]) if i <
  *               masked_m[e] (fp32 product, one rounding; a copy when
- *               row_weight is NULL), else 0.  Rows past the total untouched.
+ *               row_weight is NULL); 0 for rows the slab height dropped
+ *               (masked_m[e] <= i < psum[e] - align(psum[e-1])).  Alignment
+ *               pad rows and rows past the total are not written.
  */
 moe_status moe_masked_slab_to_expand(
     const void* slab_out, const int32_t* masked_m, int max_m, const int32_t* psum,

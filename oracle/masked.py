@@ -32,8 +32,10 @@ Readings (the bridge kernels' bodies are not on the pages):
 * Back in the expanded layout, row ``align(psum[e-1]) + i`` for i <
   masked_m[e] is ``bf16(w * slab[e * max_m + i])`` with w the row's top-k
   weight (an fp32 product, one bf16 rounding), a plain copy without weights;
-  alignment pad rows and dropped rows are zero.  The combine then sums each
-  token's rows with weight 1.
+  rows dropped by the slab height are zero (their slots still point at
+  them); alignment pad rows are not defined (no slot points at them, so the
+  combine never reads them).  The combine then sums each token's rows with
+  weight 1.
 """
 
 import numpy as np
@@ -89,12 +91,16 @@ def masked_slab_to_expand(slab_out, psum, masked_m, max_m: int, total: int, alig
                           row_weight=None):
     """Slab rows [E*max_m, H] (bf16 values as float32) -> expanded rows
     [total, H]: row start_e + i = bf16(row_weight[start_e + i] * slab[e*max_m
-    + i]) for i < masked_m[e] (a copy without weights), zeros elsewhere."""
+    + i]) for i < masked_m[e] (a copy without weights), zero for the rows the
+    slab height dropped (masked_m[e] <= i < count_e), NaN (not defined) on
+    the alignment pad rows."""
     so = np.asarray(slab_out, dtype=np.float32)
-    out = np.zeros((int(total), so.shape[1]), dtype=np.float32)
+    out = np.full((int(total), so.shape[1]), np.nan, dtype=np.float32)
     st = expert_starts(psum, align)
+    psum = np.asarray(psum, dtype=np.int64)
     for e in range(len(psum)):
         n = int(masked_m[e])
+        out[st[e] + n: psum[e]] = 0.0
         rows = so[e * max_m: e * max_m + n]
         if row_weight is not None:
             w = np.asarray(row_weight, dtype=np.float32)[st[e]: st[e] + n]

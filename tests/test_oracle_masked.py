@@ -3,8 +3,9 @@
 * The bridges' index map in closed form: slab row e * max_m + i holds
   expanded row align(psum[e-1]) + i for i < masked_m[e] = min(count_e, max_m)
   (checked by carrying row numbers through the bridge), and the way back
-  restores every live row and zeroes the pads and dropped rows; a hand case
-  of masked_m and the overflow flag.
+  restores every live row, zeroes the rows the slab height dropped and
+  leaves the alignment pads undefined; a hand case of masked_m and the
+  overflow flag.
 * The layer on the slab equals a per-token brute force with no layout or
   slab, in which each slot's down row is weighted and rounded to bf16 before
   the sum (bit-exact, fp32 and UE8M0 scales).
@@ -63,7 +64,8 @@ def test_bridge_index_map_and_round_trip(max_m):
     for e, c in enumerate(counts):
         keep = min(c, max_m)
         assert np.array_equal(back[st[e]: st[e] + keep], D[st[e]: st[e] + keep])
-        assert not back[st[e] + keep: layout.align_up(st[e] + c, align)].any()
+        assert not back[st[e] + keep: st[e] + c].any()                      # dropped
+        assert np.all(np.isnan(back[st[e] + c: layout.align_up(st[e] + c, align)]))  # pads
 
 
 def _masked_inputs(**over):
