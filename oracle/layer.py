@@ -47,6 +47,15 @@ activation quantisation); the top-k weight is applied in the gather in both
 scale formats, as that path does (no fold); the factor multiplies the fp32
 sum of the weighted rows, before the single bf16 rounding.
 
+bf16-weight path (SGLang moe_runner/deep_gemm.py source,
+``_run_bf16_contiguous_gemm``; ``pre_permute_standard_to_deep_gemm`` keeps
+the rows bf16 when the weights are bf16): the standard path's layout with
+the bf16 rows copied as they are, a bf16 grouped GEMM (gate_up, bf16 out),
+``silu_and_mul`` to bf16, the bf16 down GEMM, and the same weighted gather
+with the routed scaling factor.  Readings: each GEMM is the exact product of
+the bf16 operands rounded once to bf16 (as for the fp8 GEMMs); silu(g) * u
+is formed in fp32 as in the fp8 path and rounded once to bf16.
+
 Precision: the matmuls accumulate in float64 and round once to bf16; the
 activation and quantisation run in float32 (the precision the pages' kernels
 decide fp8 codes in); the gather accumulates in float32.
@@ -204,6 +213,95 @@ def quantize_input(x_bf16, num_valid: int, fmt: str):
         x_q[:num_valid], x_s[:num_valid] = quant.quantize_rows(
             fp8.bf16_from_bits(bits[:num_valid]), fmt)
     return x_q, x_s
+
+
+def bf16_grouped_gemm(a_bits, w_bits, m_indices, n_rows: int, live=None):
+    """out[m] = bf16(a[m] @ w[m_indices[m]]^T) with bf16 operands (uint16
+    bits), float64 products and sums, one rounding; rows that are not live or
+    labelled -1 are NaN."""
+    w_bits = np.asarray(w_bits, dtype=np.uint16)
+    out = np.full((n_rows, w_bits.shape[1]), np.nan, dtype=np.float32)
+    mi = np.asarray(m_indices)[:n_rows]
+    a_bits = np.asarray(a_bits, dtype=np.uint16)
+    for e in np.unique(mi[mi >= 0]):
+        sel = mi == e
+        if live is not None:
+            sel &= live
+        rows = np.nonzero(sel)[0]
+        if len(rows) == 0:
+            continue
+        a = fp8.bf16_from_bits(a_bits[rows]).astype(np.float64)
+        w = fp8.bf16_from_bits(w_bits[e]).astype(np.float64)
+        out[rows] = fp8.round_bf16(a @ w.T)
+    return out
+
+
+def silu_mul_bf16(G, live):
+    """bf16 silu(gate) * up of the live rows (fp32 operations, one bf16
+    rounding), as uint16 bits; other rows 0."""
+    G = np.asarray(G, dtype=np.float32)
+    n, two_i = G.shape
+    inter = two_i // 2
+    y = np.zeros((n, inter), dtype=np.uint16)
+    rows = np.nonzero(live)[0]
+    if len(rows):
+        y[rows] = fp8.bf16_bits(fp8.round_bf16(silu_mul(G[rows, :inter], G[rows, inter:])))
+    return y
+
+
+def bf16_layer(inp):
+    """The bf16-weight path: `inp` holds x_bf16 [R, H], ids, w, w13_bf16
+    [E, 2I, H], w2_bf16 [E, H, I] (uint16 bits), align, optional
+    routed_scaling_factor, num_valid and cap."""
+    from .layout import expand, capacity
+    x = np.asarray(inp["x_bf16"], dtype=np.uint16)
+    ids = np.asarray(inp["ids"])
+    R, T = ids.shape
+    E = np.asarray(inp["w13_bf16"]).shape[0]
+    align = int(inp["align"])
+    cap = int(inp.get("cap") or capacity(R, T, E, align))
+    nv = int(inp.get("num_valid", R))
+    no_scales = np.zeros((R, 0), dtype=np.float32)
+    lay = expand(ids, inp["w"], x, no_scales, nv, E, align, cap)
+    n = min(lay["total"], cap)
+    live = live_rows(lay["m_indices"], lay["psum"], align, n)
+    G = bf16_grouped_gemm(lay["ex"], inp["w13_bf16"], lay["m_indices"], n, live=live)
+    y = silu_mul_bf16(G, live)
+    D = bf16_grouped_gemm(y, inp["w2_bf16"], lay["m_indices"], n, live=live)
+    out = gather(D, lay["src2dst"], nv, topk_weights=inp["w"],
+                 scale=float(inp.get("routed_scaling_factor", 1.0)))
+    lay.update(G=G, y=y, D=D, out=out, live=live, cap=cap)
+    return lay
+
+
+def bf16_brute_force(inp, rows=None):
+    """Per-token bf16-weight path with no layout: for each slot, bf16 gate_up,
+    bf16 silu*up, bf16 down, weighted in fp32, summed in ascending k, times
+    the routed scaling factor, one bf16 rounding."""
+    x = np.asarray(inp["x_bf16"], dtype=np.uint16)
+    ids = np.asarray(inp["ids"])
+    wts = np.asarray(inp["w"], dtype=np.float32)
+    w13 = np.asarray(inp["w13_bf16"], dtype=np.uint16)
+    w2 = np.asarray(inp["w2_bf16"], dtype=np.uint16)
+    E, two_i, H = w13.shape
+    inter = two_i // 2
+    nv = int(inp.get("num_valid", len(ids)))
+    rscale = np.float32(inp.get("routed_scaling_factor", 1.0))
+    rows = list(range(nv)) if rows is None else [int(r) for r in rows]
+    out = np.zeros((len(rows), H), dtype=np.float32)
+    for i, r in enumerate(rows):
+        xr = fp8.bf16_from_bits(x[r]).astype(np.float64)
+        acc = np.zeros(H, dtype=np.float32)
+        for k in range(ids.shape[1]):
+            e = int(ids[r, k])
+            if e < 0 or e >= E:
+                continue
+            g = fp8.round_bf16(fp8.bf16_from_bits(w13[e]).astype(np.float64) @ xr)
+            y = fp8.round_bf16(silu_mul(g[:inter], g[inter:])).astype(np.float64)
+            d = fp8.round_bf16(fp8.bf16_from_bits(w2[e]).astype(np.float64) @ y)
+            acc = (acc + (d * wts[r, k]).astype(np.float32)).astype(np.float32)
+        out[i] = fp8.round_bf16((acc * rscale).astype(np.float32))
+    return out
 
 
 def standard_layer(inp):

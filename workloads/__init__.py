@@ -30,6 +30,10 @@ std_dsv3           standard single-GPU MoE of the DeepSeek-V3 shape: bf16
                    the GPU (11 GB of fp8 weights), top-8 uniform,
                    alignment 128, fp32 scales, routed scaling factor 2.5
                    (the model's own)
+std_bf16_tiny      standard path with bf16 weights (no quantisation
+                   anywhere): std_tiny's shape
+std_dsv3_bf16      standard single-GPU MoE, DeepSeek-V3 shape, bf16
+                   weights (256 experts, 22.5 GB), factor 2.5
 dsv3_decode        decode share on the masked slab: 1024 received rows
                    (32 tokens from each of 32 source ranks), H=7168,
                    I=2048, 8 local of 256 experts, top-8 uniform,
@@ -70,6 +74,7 @@ class Workload:
     input: str = "fp8"      # 'fp8' (received, quantised) or 'bf16' (standard path)
     routed_scale: float = 1.0   # routed scaling factor applied in the gather
     max_m: int = 0          # >0: decode path on a masked slab of this height
+    weights: str = "fp8"    # 'fp8' (block-scaled) or 'bf16' (bf16 GEMMs, no quantisation)
     extra: dict = field(default_factory=dict)
 
 
@@ -91,6 +96,10 @@ WORKLOADS = {
                          input="bf16", routed_scale=2.5),
     "std_dsv3": Workload("std_dsv3", 4096, 7168, 2048, 256, 256, 8, 128,
                          seed=1007, input="bf16", routed_scale=2.5),
+    "std_bf16_tiny": Workload("std_bf16_tiny", 64, 256, 128, 8, 8, 2, 64, seed=1009,
+                              input="bf16", routed_scale=2.5, weights="bf16"),
+    "std_dsv3_bf16": Workload("std_dsv3_bf16", 4096, 7168, 2048, 256, 256, 8, 128,
+                              seed=1010, input="bf16", routed_scale=2.5, weights="bf16"),
     "dsv3_decode": Workload("dsv3_decode", 1024, 7168, 2048, 8, 256, 8, 128,
                             seed=1008, max_m=128),
 }
