@@ -27,6 +27,7 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0        # MI355X HBM3E
 FP8_PEAK_TFLOPS = 5000.0     # MI355X dense fp8 MFMA
+BF16_PEAK_TFLOPS = 2500.0    # MI355X dense bf16 MFMA
 METRIC = "expanded MoE layer tokens/s per GPU (DSv3 shape); HBM GB/s & MFMA util vs peak"
 
 
@@ -100,6 +101,22 @@ def make_weights(wl, device, gen):
     return w13q, w13s, w2q, w2s
 
 
+def make_weights_bf16(wl, device, gen):
+    """bf16 w13 [E, 2I, H] and w2 [E, H, I] ~ N(0, 0.02), a few experts at a time."""
+    import torch
+    E, H, I = wl.experts, wl.hidden, wl.inter
+    w13 = torch.empty((E, 2 * I, H), dtype=torch.bfloat16, device=device)
+    w2 = torch.empty((E, H, I), dtype=torch.bfloat16, device=device)
+    step = 16
+    for e0 in range(0, E, step):
+        e1 = min(E, e0 + step)
+        w13[e0:e1] = (torch.randn((e1 - e0, 2 * I, H), generator=gen, device=device)
+                      * 0.02).to(torch.bfloat16)
+        w2[e0:e1] = (torch.randn((e1 - e0, H, I), generator=gen, device=device)
+                     * 0.02).to(torch.bfloat16)
+    return w13, w2
+
+
 def make_inputs(wl, device):
     import numpy as np
     import torch
@@ -109,6 +126,14 @@ def make_inputs(wl, device):
     gen.manual_seed(wl.seed)
     R, H, I, E = wl.rows, wl.hidden, wl.inter, wl.experts
     x = torch.randn((R, H), generator=gen, device=device, dtype=torch.float32)
+    if wl.weights == "bf16":    # bf16-weight path: nothing is quantised
+        xb = x.to(torch.bfloat16)
+        del x
+        w13, w2 = make_weights_bf16(wl, device, gen)
+        torch.cuda.synchronize()
+        return dict(x=xb, x_scale=None, ids=torch.from_numpy(d["ids"]).to(device),
+                    w=torch.from_numpy(d["w"]).to(device), prank=None, w13=w13,
+                    w13_scale=None, w2=w2, w2_scale=None, num_valid=d["num_valid"], data=d)
     if wl.input == "bf16":      # standard path: bf16 token rows, quantised by the layout
         xb = x.to(torch.bfloat16)
         del x
@@ -159,12 +184,13 @@ def measured_traffic(workload):
     return int(rec["traffic_bytes_per_launch"])
 
 
-def gemm_cost(rows, n, k, nonempty, sbytes):
+def gemm_cost(rows, n, k, nonempty, sbytes, eb=1):
     """Algorithmic HBM bytes and useful flops of one grouped GEMM launch: each
-    non-empty expert's weights and block scales once, the live rows' fp8
-    activations and scales once, their bf16 outputs once."""
-    weights = nonempty * (n * k + (n // 128) * (k // 128) * sbytes)
-    acts = rows * (k + (k // 128) * sbytes)
+    non-empty expert's weights and block scales once, the live rows'
+    activations and scales once, their bf16 outputs once (eb: bytes per
+    operand value, 1 for fp8, 2 for bf16)."""
+    weights = nonempty * (n * k * eb + (n // 128) * (k // 128) * sbytes)
+    acts = rows * (k * eb + (k // 128) * sbytes)
     return weights + acts + rows * n * 2, 2.0 * rows * n * k
 
 
@@ -221,7 +247,11 @@ def main():
     inp = make_inputs(wl, dev)
     std = wl.input == "bf16"
     masked = wl.max_m > 0
-    if masked:
+    wbf = wl.weights == "bf16"
+    if wbf:
+        mod = M.StandardBf16MoE(wl.rows, wl.topk, inp["w13"], inp["w2"], wl.align,
+                                wl.routed_scale, device=dev)
+    elif masked:
         mod = M.MaskedMoE(wl.rows, wl.topk, inp["w13"], inp["w13_scale"], inp["w2"],
                           inp["w2_scale"], wl.align, wl.max_m, wl.fmt, device=dev)
     elif std:
@@ -231,7 +261,7 @@ def main():
         mod = M.ExpandedMoE(wl.rows, wl.topk, inp["w13"], inp["w13_scale"], inp["w2"],
                             inp["w2_scale"], wl.align, wl.fmt, device=dev)
     out = torch.empty((wl.rows, wl.hidden), dtype=torch.bfloat16, device=dev)
-    fold = mod.row_weight if wl.fmt == "f32" and not std else None
+    fold = mod.row_weight if wl.fmt == "f32" and not std and not wbf else None
 
     def layout_stage():
         if std:
@@ -239,7 +269,18 @@ def main():
         else:
             mod.layout(inp["x"], inp["x_scale"], inp["ids"], inp["w"], inp["prank"])
 
-    if masked:   # decode path: bridges into and out of the masked slab
+    if wbf:      # bf16 weights: no quantisation anywhere
+        stage_list = [
+            ("expand_layout", layout_stage),
+            ("gemm_gate_up", lambda: M.moe_grouped_gemm_bf16(
+                mod.ex, mod.w13, mod.psum, mod.status, wl.align, mod.gate_up)),
+            ("act_quant", lambda: M.moe_silu_mul_bf16(
+                mod.gate_up, mod.m_indices, mod.psum, mod.status, mod.E, wl.align, mod.y)),
+            ("gemm_down", lambda: M.moe_grouped_gemm_bf16(
+                mod.y, mod.w2, mod.psum, mod.status, wl.align, mod.down)),
+            ("gather", lambda: mod.gather(inp["w"], inp["prank"], out)),
+        ]
+    elif masked:   # decode path: bridges into and out of the masked slab
         mm = wl.max_m
         stage_list = [
             ("expand_layout", layout_stage),
@@ -345,23 +386,25 @@ def main():
     m_used = int(status[0])
     nonempty = int((counts > 0).sum())
     H, I = wl.hidden, wl.inter
-    sb = 4 if wl.fmt == "f32" else 1
+    sb = 0 if wbf else (4 if wl.fmt == "f32" else 1)
+    eb = 2 if wbf else 1
+    peak_tf = BF16_PEAK_TFLOPS if wbf else FP8_PEAK_TFLOPS
     # Dominant kernel: the grouped GEMM, averaged over its two launches per
     # step (gate_up [A, 2I] x K=H, then down [A, H] x K=I; A = live rows).
-    g1_bytes, g1_flops = gemm_cost(A, 2 * I, H, nonempty, sb)
-    g2_bytes, g2_flops = gemm_cost(A, H, I, nonempty, sb)
+    g1_bytes, g1_flops = gemm_cost(A, 2 * I, H, nonempty, sb, eb)
+    g2_bytes, g2_flops = gemm_cost(A, H, I, nonempty, sb, eb)
     t = (gemm1_us + gemm2_us) * 1e-6
     byts, flops = g1_bytes + g2_bytes, g1_flops + g2_flops
-    if byts / (HBM_PEAK_GBS * 1e9) >= flops / (FP8_PEAK_TFLOPS * 1e12):
+    if byts / (HBM_PEAK_GBS * 1e9) >= flops / (peak_tf * 1e12):
         roof = {"bound": "hbm", "achieved": byts / t / 1e9, "peak": HBM_PEAK_GBS,
                 "unit": "GB/s"}
     else:
-        roof = {"bound": "mfma", "achieved": flops / t / 1e12, "peak": FP8_PEAK_TFLOPS,
+        roof = {"bound": "mfma", "achieved": flops / t / 1e12, "peak": peak_tf,
                 "unit": "TFLOP/s"}
     roof["frac"] = roof["achieved"] / roof["peak"]
     roof["traffic"] = measured_traffic(wl.name)
-    roof["kernel"] = (f"grouped_gemm_kernel<{str(wl.fmt == 'ue8m0').lower()}, "
-                      f"{str(masked).lower()}> "
+    roof["kernel"] = (f"grouped_gemm_kernel<{'bf16' if wbf else ('ue8m0' if wl.fmt == 'ue8m0' else 'fp32-scale fp8')}, "
+                      f"{'masked' if masked else 'contiguous'}> "
                       "(mean over its gate_up and down launches)")
     roof["launch_us"] = {"gate_up": gemm1_us, "down": gemm2_us, "mean": (gemm1_us + gemm2_us) / 2}
     roof["algorithmic_bytes_per_launch"] = byts / 2
@@ -375,13 +418,14 @@ def main():
     R, T, nv, E = wl.rows, wl.topk, inp["num_valid"], wl.experts
     sH, sI = (H // 128) * sb, (I // 128) * sb
     row_in = 2 * H if std else H + sH   # a received row: bf16, or fp8 + scales
+    row_ex = 2 * H if wbf else H + sH   # an expanded row: kept bf16, or fp8 + scales
     ids_v = inp["data"]["ids"][:nv]
     r_live = int(((ids_v >= 0) & (ids_v < E)).any(axis=1).sum())   # rows read by the scatter
     st_bytes = {
-        "expand_layout": nv * T * 8 + r_live * row_in + m_used * (H + sH + 4) + R * T * 4
-                         + mod.capacity * 4,
+        "expand_layout": nv * T * 8 + r_live * row_in + m_used * row_ex
+                         + (0 if wbf else m_used * 4) + R * T * 4 + mod.capacity * 4,
         "gemm_gate_up": g1_bytes,
-        "act_quant": A * 4 * I + (A if masked else m_used) * (I + sI),
+        "act_quant": A * 4 * I + (A * 2 * I if wbf else (A if masked else m_used) * (I + sI)),
         "gemm_down": g2_bytes,
         "gather": A * 2 * H + nv * 2 * H + nv * T * 8,
         # bridges of the masked slab: live rows + scales copied in; the live
@@ -398,11 +442,11 @@ def main():
         if n in st_flops:
             rec["flops"] = st_flops[n]
             rec["tflops"] = st_flops[n] / us / 1e6
-            rec["mfma_frac"] = rec["tflops"] / FP8_PEAK_TFLOPS
+            rec["mfma_frac"] = rec["tflops"] / peak_tf
         stages[n] = rec
 
     cpu = None
-    if not args.no_cpu_baseline and not std and not masked:
+    if not args.no_cpu_baseline and not std and not masked and not wbf:
         cpu = cpu_baseline(inp, wl, args.cpu_runs)
 
     res = {
@@ -416,14 +460,15 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "fp8_e4m3 (fp32 accumulate, bf16 out)",
+        "dtype": "bf16 (fp32 accumulate)" if wbf else "fp8_e4m3 (fp32 accumulate, bf16 out)",
         "data": "synthetic (seeded; routing/weights per the workload recipe)",
         "config": {"workload": wl.name, "input": wl.input, "routed_scaling_factor": wl.routed_scale,
                    "masked_slab_max_m": wl.max_m,
                    "rows": wl.rows, "valid_rows": inp["num_valid"],
                    "hidden": H, "inter": I, "experts_local": wl.experts,
                    "experts_global": wl.global_experts, "topk": wl.topk,
-                   "align": wl.align, "scale_fmt": wl.fmt, "parallelism": "ep-rank share, 1 GPU",
+                   "align": wl.align, "scale_fmt": "none" if wbf else wl.fmt,
+                   "weights": wl.weights, "parallelism": "ep-rank share, 1 GPU",
                    "assignments": A, "expanded_rows": m_used, "capacity": mod.capacity},
         "stages_us": stages_us,
         "stages": stages,

@@ -10,13 +10,15 @@ Functions mirror the C ABI in ``include/moe_expand.h``:
     moe_expand_layout, moe_expand_layout_bf16, moe_grouped_gemm_fp8,
     moe_act_quant, moe_gather, moe_expand_to_masked_slab,
     moe_grouped_gemm_fp8_masked, moe_act_quant_masked, moe_masked_slab_to_expand,
+    moe_grouped_gemm_bf16, moe_silu_mul_bf16,
     moe_expand_capacity, moe_expand_workspace_bytes, moe_status_string
 
 plus :class:`ExpandedMoE`, which allocates the buffers once for a given
 receive-buffer size and runs the five calls of a layer in order, and
 :class:`StandardMoE`, the same for the standard (non-EP) path: bf16 token
 rows in, top-k weights and the routed scaling factor applied in the gather,
-and :class:`MaskedMoE`, the decode path on a fixed-height masked slab.
+:class:`MaskedMoE`, the decode path on a fixed-height masked slab, and
+:class:`StandardBf16MoE`, the standard path with bf16 weights.
 """
 
 import ctypes
@@ -29,9 +31,9 @@ HEADER_PATH = os.path.join(os.path.dirname(_HERE), "include", "moe_expand.h")
 
 MOE_OK, MOE_ERR_NULL, MOE_ERR_SHAPE, MOE_ERR_ALIGNMENT = 0, 1, 2, 3
 MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE, MOE_ERR_LAUNCH = 4, 5, 6
-MOE_SCALE_F32, MOE_SCALE_UE8M0 = 0, 1
+MOE_SCALE_F32, MOE_SCALE_UE8M0, MOE_SCALE_NONE = 0, 1, 2
 MOE_FLAG_CAPACITY_OVERFLOW, MOE_FLAG_EXPERT_ID_RANGE, MOE_FLAG_SLAB_OVERFLOW = 1, 2, 4
-FMT = {"f32": MOE_SCALE_F32, "ue8m0": MOE_SCALE_UE8M0}
+FMT = {"f32": MOE_SCALE_F32, "ue8m0": MOE_SCALE_UE8M0, "none": MOE_SCALE_NONE}
 
 _P = ctypes.c_void_p
 _I64 = ctypes.c_int64
@@ -55,6 +57,8 @@ _SIGNATURES = {
     "moe_grouped_gemm_fp8_masked": (_I, [_P, _P, _I, _P, _P, _P, _I, _I, _I, _I, _P, _P]),
     "moe_act_quant_masked": (_I, [_P, _P, _I, _I, _I, _I, _P, _P, _P]),
     "moe_masked_slab_to_expand": (_I, [_P, _P, _I, _P, _P, _P, _P, _I64, _I, _I, _I, _P, _P]),
+    "moe_grouped_gemm_bf16": (_I, [_P, _P, _P, _P, _I64, _I, _I, _I, _I, _P, _P]),
+    "moe_silu_mul_bf16": (_I, [_P, _P, _P, _P, _I64, _I, _I, _I, _P, _P]),
 }
 
 _lib = None
@@ -234,6 +238,24 @@ def moe_masked_slab_to_expand(slab_out, masked_m, max_m, psum, status, m_indices
     _check("moe_masked_slab_to_expand", code)
 
 
+def moe_grouped_gemm_bf16(a, w, psum, status, align, out, stream=None):
+    """a [capacity, k] bf16, w [E, n, k] bf16 -> out [capacity, n] bf16."""
+    capacity, k = a.shape
+    E, n, _ = w.shape
+    code = lib().moe_grouped_gemm_bf16(_ptr(a), _ptr(w), _ptr(psum), _ptr(status), capacity,
+                                       n, k, E, align, _ptr(out), _stream(stream))
+    _check("moe_grouped_gemm_bf16", code)
+
+
+def moe_silu_mul_bf16(gate_up, m_indices, psum, status, num_experts, align, out, stream=None):
+    """gate_up [capacity, 2I] bf16 -> out [capacity, I] bf16 (live rows)."""
+    capacity, two_i = gate_up.shape
+    code = lib().moe_silu_mul_bf16(_ptr(gate_up), _ptr(m_indices), _ptr(psum), _ptr(status),
+                                   capacity, two_i // 2, num_experts, align, _ptr(out),
+                                   _stream(stream))
+    _check("moe_silu_mul_bf16", code)
+
+
 class ExpandedMoE:
     """Buffers for one receive-buffer size, and the layer's five calls.
 
@@ -381,3 +403,60 @@ class MaskedMoE(ExpandedMoE):
 
     def gather(self, topk_weights, psum_recv_per_rank, out, stream=None):
         moe_gather(self.down, self.src2dst, None, psum_recv_per_rank, out, stream)
+
+
+class StandardBf16MoE:
+    """The standard path with bf16 weights: bf16 token rows scattered as they
+    are into the 128-aligned expert blocks, bf16 gate_up GEMM, SiLU*up to
+    bf16, bf16 down GEMM, gather with the top-k weights and the routed
+    scaling factor.  w13 [E, 2I, H], w2 [E, H, I] bf16."""
+
+    def __init__(self, rows, topk, w13, w2, align=128, routed_scaling_factor=1.0,
+                 device="cuda"):
+        import torch
+        self.w13, self.w2, self.align = w13, w2, align
+        self.routed_scaling_factor = float(routed_scaling_factor)
+        E, two_i, H = w13.shape
+        self.E, self.I, self.H = E, two_i // 2, H
+        self.rows, self.topk = rows, topk
+        cap = moe_expand_capacity(rows, topk, E, align)
+        self.capacity = cap
+        bf, i32 = torch.bfloat16, torch.int32
+        self.ex = torch.empty((cap, H), dtype=bf, device=device)
+        self.psum = torch.empty(E, dtype=i32, device=device)
+        self.m_indices = torch.empty(cap, dtype=i32, device=device)
+        self.src2dst = torch.empty((rows, topk), dtype=i32, device=device)
+        self.status = torch.empty(2, dtype=i32, device=device)
+        wsb = moe_expand_workspace_bytes(rows, topk, E)
+        self.workspace = torch.empty(max(wsb, 256), dtype=torch.uint8, device=device)
+        self.gate_up = torch.empty((cap, 2 * self.I), dtype=bf, device=device)
+        self.y = torch.empty((cap, self.I), dtype=bf, device=device)
+        self.down = torch.empty((cap, H), dtype=bf, device=device)
+
+    def layout(self, x, topk_ids, topk_weights, psum_recv_per_rank=None, stream=None):
+        moe_expand_layout_bf16(x, "none", topk_ids, topk_weights, psum_recv_per_rank, self.E,
+                               self.align, self.capacity, self.ex, None, self.psum,
+                               self.m_indices, self.src2dst, None, self.status,
+                               self.workspace, stream)
+
+    def experts(self, stream=None):
+        moe_grouped_gemm_bf16(self.ex, self.w13, self.psum, self.status, self.align,
+                              self.gate_up, stream)
+        moe_silu_mul_bf16(self.gate_up, self.m_indices, self.psum, self.status, self.E,
+                          self.align, self.y, stream)
+        moe_grouped_gemm_bf16(self.y, self.w2, self.psum, self.status, self.align, self.down,
+                              stream)
+
+    def gather(self, topk_weights, psum_recv_per_rank, out, stream=None):
+        moe_gather(self.down, self.src2dst, topk_weights, psum_recv_per_rank, out, stream,
+                   routed_scaling_factor=self.routed_scaling_factor)
+
+    def __call__(self, x, topk_ids, topk_weights, psum_recv_per_rank=None, out=None,
+                 stream=None):
+        import torch
+        if out is None:
+            out = torch.empty((self.rows, self.H), dtype=torch.bfloat16, device=x.device)
+        self.layout(x, topk_ids, topk_weights, psum_recv_per_rank, stream)
+        self.experts(stream)
+        self.gather(topk_weights, psum_recv_per_rank, out, stream)
+        return out

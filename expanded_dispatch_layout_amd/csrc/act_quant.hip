@@ -29,7 +29,11 @@ __device__ __forceinline__ float silu_mul(float g, float u) {
 // kMasked (the decode path's slab, rows e * max_m + i): `m_indices` is
 // masked_m, `psum` and `status` are unused, capacity = E * max_m; rows with
 // i >= masked_m[e] are neither read nor written (nothing reads them).
-template <bool kUe8m0, bool kFold, bool kMasked>
+// kBfOut (the bf16-weight path, SGLang moe_runner/deep_gemm.py source,
+// _run_bf16_contiguous_gemm: silu_and_mul to bf16 between the bf16 GEMMs):
+// y is rounded to bf16 and stored to `out` as [capacity, inter] bf16, with no
+// quantisation; pad rows are not written (the GEMM never reads them).
+template <bool kUe8m0, bool kFold, bool kMasked, bool kBfOut = false>
 __global__ __launch_bounds__(kThreads) void act_quant_kernel(
     const uint16_t* __restrict__ gu, const int32_t* __restrict__ m_indices,
     const int32_t* __restrict__ psum, const int32_t* __restrict__ status, int64_t capacity,
@@ -64,6 +68,27 @@ __global__ __launch_bounds__(kThreads) void act_quant_kernel(
       uv0 = *reinterpret_cast<const u32x4*>(grow + inter + t * 8);
     }
     uint8_t* qrow = out + m * inter;
+    if constexpr (kBfOut) {
+      if (m >= pe) continue;  // alignment pad row: never read
+      uint16_t* brow = reinterpret_cast<uint16_t*>(out) + m * inter;
+      for (int c0 = 0; c0 < inter; c0 += kThreads * 8) {
+        const int col = c0 + t * 8;
+        if (col >= inter) continue;
+        const u32x4 gv = c0 == 0 ? gv0 : *reinterpret_cast<const u32x4*>(grow + col);
+        const u32x4 uv = c0 == 0 ? uv0 : *reinterpret_cast<const u32x4*>(grow + inter + col);
+        u32x4 o;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const float lo =
+              silu_mul(__uint_as_float(gv[i] << 16), __uint_as_float(uv[i] << 16));
+          const float hi = silu_mul(__uint_as_float(gv[i] & 0xffff0000u),
+                                    __uint_as_float(uv[i] & 0xffff0000u));
+          o[i] = (uint32_t)f32_to_bf16_rne(lo) | ((uint32_t)f32_to_bf16_rne(hi) << 16);
+        }
+        *reinterpret_cast<u32x4*>(brow + col) = o;
+      }
+      continue;
+    }
     // out_scale is K-block-major: scale (row m, group g) at g * capacity + m.
     if (m >= pe) {  // alignment pad row: zeros
       for (int c = t; c < inter / 16; c += kThreads)
@@ -155,6 +180,29 @@ extern "C" moe_status moe_act_quant(const void* gate_up, const int32_t* m_indice
   hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(kThreads), 0, s, (const uint16_t*)gate_up,
                      m_indices, psum, status, capacity, inter, num_experts, 0, fold_weight,
                      (uint8_t*)out, (uint8_t*)out_scale);
+  if (hipGetLastError() != hipSuccess) return MOE_ERR_LAUNCH;
+  return MOE_OK;
+}
+
+extern "C" moe_status moe_silu_mul_bf16(const void* gate_up, const int32_t* m_indices,
+                                        const int32_t* psum, const int32_t* status,
+                                        int64_t capacity, int inter, int num_experts, int align,
+                                        void* out, void* stream) {
+  if (capacity < 0 || capacity > (1LL << 30) || inter <= 0 || inter % 8 != 0 ||
+      num_experts < 1 || num_experts > MOE_MAX_EXPERTS)
+    return MOE_ERR_SHAPE;
+  if (align < MOE_MIN_ALIGN || align > MOE_MAX_ALIGN || (align & (align - 1)))
+    return MOE_ERR_UNSUPPORTED;
+  if (capacity % align != 0) return MOE_ERR_SHAPE;
+  if (!m_indices || !psum || !status) return MOE_ERR_NULL;
+  if (capacity > 0 && (!gate_up || !out)) return MOE_ERR_NULL;
+  if (((uintptr_t)gate_up % 16) || ((uintptr_t)out % 16)) return MOE_ERR_ALIGNMENT;
+  if (capacity == 0) return MOE_OK;
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  int64_t grid = capacity < 2048 ? capacity : 2048;
+  hipLaunchKernelGGL((act_quant_kernel<false, false, false, true>), dim3((unsigned)grid),
+                     dim3(kThreads), 0, s, (const uint16_t*)gate_up, m_indices, psum, status,
+                     capacity, inter, num_experts, 0, nullptr, (uint8_t*)out, nullptr);
   if (hipGetLastError() != hipSuccess) return MOE_ERR_LAUNCH;
   return MOE_OK;
 }

@@ -58,6 +58,10 @@ namespace {
 typedef int v8i __attribute__((ext_vector_type(8)));
 typedef float v4f __attribute__((ext_vector_type(4)));
 
+// Operand formats: fp8 with fp32 scales (promoted in VALU), fp8 with UE8M0
+// scales (the MFMA's own scale operands), bf16 (no scales).
+constexpr int kF32 = 0, kU8 = 1, kBF = 2;
+
 constexpr int kThreads = 512;  // 8 waves: 2 per SIMD
 constexpr int kWaves = kThreads / 64;
 constexpr int kXcds = 8;       // MI355X: 8 XCDs, workgroups dispatched round-robin
@@ -281,12 +285,12 @@ struct WaveLoads {
     for (int j = 0; j < B_LOADS; ++j) dma16(src, off[j], lds + lds_off[j]);
   }
   // Activations (NA loads) and the scale load of one stage.
-  template <int NA>
+  template <int NA, bool kScales>
   __device__ __forceinline__ void acts(const uint8_t* src, uint32_t lds, const uint8_t* ssrc,
                                        uint32_t slds) const {
 #pragma unroll
     for (int j = 0; j < NA; ++j) dma16(src, off[j], lds + lds_off[j]);
-    dma4(ssrc, scale_off, dummy ? dummy : slds + scale_rel);
+    if constexpr (kScales) dma4(ssrc, scale_off, dummy ? dummy : slds + scale_rel);
   }
 };
 
@@ -334,10 +338,16 @@ __device__ __forceinline__ v4f mfma_plain(const v8i& a, const v8i& b) {
 // fp32 scales early in the step itself (the first promotion comes two MFMAs
 // in), for UE8M0 at the end of the step before (the MFMAs take them as
 // operands).
-template <bool kUe8m0, int NFM>
+template <int kFmt, int NFM>
 struct StepScales;
 template <int NFM>
-struct StepScales<false, NFM> {
+struct StepScales<kBF, NFM> {  // bf16: no scales
+  __device__ __forceinline__ void read(uint32_t, uint32_t, const Item&, const FragOffsets&, int,
+                                       int) {}
+  __device__ __forceinline__ void finish(const Item&, const FragOffsets&, int, int) {}
+};
+template <int NFM>
+struct StepScales<kF32, NFM> {
   float raw[NFM];  // activation scale of this lane's row, per row tile
   float wraw;      // the weight block scale
   float scl[NFM];  // their products
@@ -353,7 +363,7 @@ struct StepScales<false, NFM> {
   }
 };
 template <int NFM>
-struct StepScales<true, NFM> {
+struct StepScales<kU8, NFM> {
   uint32_t raw[NFM];  // row r's exponent byte is byte r of the slot
   uint32_t wraw;
   int abyte[NFM];
@@ -385,9 +395,9 @@ struct StepScales<true, NFM> {
 // loads for a later stage) runs in the shadow of the first MFMAs instead of
 // delaying them.  NFM: how many of the wave's four 16-row tiles hold live
 // rows.
-template <bool kUe8m0, int NFM, bool kNext, typename Issue>
+template <int kFmt, int NFM, bool kNext, typename Issue>
 __device__ __forceinline__ void step(v8i (&a)[FM], v8i (&b)[FN], v4f (&acc)[FM][FN],
-                                     StepScales<kUe8m0, NFM>& ss, uint32_t next_a,
+                                     StepScales<kFmt, NFM>& ss, uint32_t next_a,
                                      uint32_t next_b, uint32_t next_sc, uint32_t bsc,
                                      const Item& it, const FragOffsets& fo, int kb, int lane,
                                      Issue&& issue) {
@@ -401,14 +411,44 @@ __device__ __forceinline__ void step(v8i (&a)[FM], v8i (&b)[FN], v4f (&acc)[FM][
   };
   auto side = [&](int t) __attribute__((always_inline)) {  // after MFMA t: work not feeding this step
     if (t == 0) {
-      if constexpr (!kUe8m0) ss.finish(it, fo, kb, lane);    // this step's products
+      if constexpr (kFmt == kF32) ss.finish(it, fo, kb, lane);  // this step's products
       if constexpr (kNext) ss.read(next_sc, bsc, it, fo, kb + 1, lane);
     }
-    if constexpr (kUe8m0 && kNext)
+    if constexpr (kFmt == kU8 && kNext)
       if (t == M - 1) ss.finish(it, fo, kb + 1, lane);       // the next step's operands
     if (t == (M > 1 ? 1 : 0)) issue();
   };
-  if constexpr (kUe8m0) {
+  if constexpr (kFmt == kBF) {
+    // bf16: a 128-byte K step is 64 values, two 16x16x32 MFMAs per tile on
+    // the fragments' two 16-byte halves (A and B split K the same way, so
+    // the two products cover the step's K exactly once).  All first halves,
+    // then all second halves: the two MFMAs of one accumulator are M slots
+    // apart.  The fragments are replaced after their second use.
+    typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+    auto half = [](const v8i& f, int h) __attribute__((always_inline)) {
+      typedef int v4i __attribute__((ext_vector_type(4)));
+      const v4i q = h ? v4i{f[4], f[5], f[6], f[7]} : v4i{f[0], f[1], f[2], f[3]};
+      return __builtin_bit_cast(bf16x8, q);
+    };
+#pragma unroll
+    for (int t = 0; t < M; ++t) {
+      const int i = t / FN, j = t % FN;
+      acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(half(b[j], 0), half(a[i], 0),
+                                                          acc[i][j], 0, 0, 0);
+      sched_fence();
+      side(t);
+      sched_fence();
+    }
+#pragma unroll
+    for (int t = 0; t < M; ++t) {
+      const int i = t / FN, j = t % FN;
+      acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(half(b[j], 1), half(a[i], 1),
+                                                          acc[i][j], 0, 0, 0);
+      sched_fence();
+      refresh(t);
+      sched_fence();
+    }
+  } else if constexpr (kFmt == kU8) {
     // The exponent bytes are the MFMA's own scale operands.
 #pragma unroll
     for (int t = 0; t < M; ++t) {
@@ -457,12 +497,13 @@ __device__ __forceinline__ void step(v8i (&a)[FM], v8i (&b)[FN], v4f (&acc)[FM][
 // registers, so the slots of stage kb are free); refill them with the next
 // stage of the stream; compute step kb from registers while reading step
 // kb+1's fragments.
-template <bool kUe8m0, int NFM, int ROLE>
+template <int kFmt, int NFM, int ROLE>
 __device__ __forceinline__ void kloop(uint32_t lds0, v4f (&acc)[FM][FN], const Item& it,
                                       const WaveLoads& wl, const FragOffsets& fo, int lane,
                                       int wid) {
   constexpr bool kW = ROLE == 0;
-  constexpr int NL = kW ? W_LOADS : ROLE + 1;         // loads per stage
+  constexpr bool kSc = kFmt != kBF;                   // activation scales streamed
+  constexpr int NL = kW ? W_LOADS : ROLE + (kSc ? 1 : 0);  // loads per stage
   constexpr int D = kW ? kBSlots : act_slots(ROLE);   // stream depth (slots)
   const int KB = it.KB;
   const uint32_t a_end = lds0 + A_BASE + (uint32_t)(it.na_slots * it.a_slot_bytes);
@@ -476,7 +517,7 @@ __device__ __forceinline__ void kloop(uint32_t lds0, v4f (&acc)[FM][FN], const I
       wl.weights(src, dst);
       dst = dst + B_BYTES == lds0 + B_RING ? lds0 : dst + B_BYTES;
     } else {
-      wl.template acts<ROLE>(src, dst, ssrc, sdst);
+      wl.template acts<ROLE, kSc>(src, dst, ssrc, sdst);
       dst = dst + it.a_slot_bytes == a_end ? lds0 + A_BASE : dst + it.a_slot_bytes;
       sdst = sdst + SC_SLOT == lds0 + SC_BASE + kScSlots * SC_SLOT ? lds0 + SC_BASE
                                                                     : sdst + SC_SLOT;
@@ -490,7 +531,8 @@ __device__ __forceinline__ void kloop(uint32_t lds0, v4f (&acc)[FM][FN], const I
 
   // The item's weight block scales: issued before this wave's stage 0, so
   // the prologue's wait for stage 0 covers them too (loads complete in order).
-  if (wid == kWaves - 1) load_item_wscales(it, lds0, lane);
+  if constexpr (kSc)
+    if (wid == kWaves - 1) load_item_wscales(it, lds0, lane);
   // Prologue: stages 0..D-2 of the stream, wait for stage 0 with the rest
   // in flight; after the barrier, read stage 0's fragments and issue the
   // stream's next stage into the last free slot.
@@ -499,7 +541,7 @@ __device__ __forceinline__ void kloop(uint32_t lds0, v4f (&acc)[FM][FN], const I
   wait_ahead<NL, D - 2>(pre - 1);
   barrier();
   v8i a[FM], b[FN];
-  StepScales<kUe8m0, NFM> ss;
+  StepScales<kFmt, NFM> ss;
   if constexpr (NFM > 0) {
 #pragma unroll
     for (int j = 0; j < FN; ++j) b[j] = frag2(lds0 + j * 2048, fo.b_lo, fo.b_hi);
@@ -507,7 +549,7 @@ __device__ __forceinline__ void kloop(uint32_t lds0, v4f (&acc)[FM][FN], const I
     for (int i = 0; i < NFM; ++i)
       a[i] = frag2(lds0 + A_BASE + i * A_TILE_STRIDE, fo.a_lo, fo.a_hi);
     ss.read(lds0 + SC_BASE, bsc, it, fo, 0, lane);
-    if constexpr (kUe8m0) ss.finish(it, fo, 0, lane);
+    if constexpr (kFmt == kU8) ss.finish(it, fo, 0, lane);
   }
   if (pre < KB) issue();  // stages 0 .. min(D, KB) - 1 are now in flight
   // Read-side slot of stage kb+1's scales.
@@ -520,7 +562,7 @@ __device__ __forceinline__ void kloop(uint32_t lds0, v4f (&acc)[FM][FN], const I
     wait_lgkm0();
     barrier();
     if constexpr (NFM > 0) {
-      step<kUe8m0, NFM, true>(a, b, acc, ss, ra, rb, rsn, bsc, it, fo, kb, lane, issue_fn);
+      step<kFmt, NFM, true>(a, b, acc, ss, ra, rb, rsn, bsc, it, fo, kb, lane, issue_fn);
     } else {
       issue_fn();
     }
@@ -539,30 +581,30 @@ __device__ __forceinline__ void kloop(uint32_t lds0, v4f (&acc)[FM][FN], const I
     body(kb, [&] { wait_ahead<NL, D - 2>(KB - kb - 2); }, [] {});
   // Last step: nothing left to read ahead or load.
   if constexpr (NFM > 0)
-    step<kUe8m0, NFM, false>(a, b, acc, ss, 0u, 0u, 0u, bsc, it, fo, KB - 1, lane, [] {});
+    step<kFmt, NFM, false>(a, b, acc, ss, 0u, 0u, 0u, bsc, it, fo, KB - 1, lane, [] {});
 }
 
 // The K loop instantiation for this wave's live-tile count and role.
-template <bool kUe8m0, int NFM>
+template <int kFmt, int NFM>
 __device__ __forceinline__ void kloop_role(int role, uint32_t lds0, v4f (&acc)[FM][FN],
                                            const Item& it, const WaveLoads& wl,
                                            const FragOffsets& fo, int lane, int wid) {
   switch (role) {  // uniform per wave
-    case 0: kloop<kUe8m0, NFM, 0>(lds0, acc, it, wl, fo, lane, wid); break;
-    case 1: kloop<kUe8m0, NFM, 1>(lds0, acc, it, wl, fo, lane, wid); break;
-    case 2: kloop<kUe8m0, NFM, 2>(lds0, acc, it, wl, fo, lane, wid); break;
-    case 3: kloop<kUe8m0, NFM, 3>(lds0, acc, it, wl, fo, lane, wid); break;
-    case 4: kloop<kUe8m0, NFM, 4>(lds0, acc, it, wl, fo, lane, wid); break;
-    case 5: kloop<kUe8m0, NFM, 5>(lds0, acc, it, wl, fo, lane, wid); break;
-    case 6: kloop<kUe8m0, NFM, 6>(lds0, acc, it, wl, fo, lane, wid); break;
-    case 7: kloop<kUe8m0, NFM, 7>(lds0, acc, it, wl, fo, lane, wid); break;
-    default: kloop<kUe8m0, NFM, 8>(lds0, acc, it, wl, fo, lane, wid); break;
+    case 0: kloop<kFmt, NFM, 0>(lds0, acc, it, wl, fo, lane, wid); break;
+    case 1: kloop<kFmt, NFM, 1>(lds0, acc, it, wl, fo, lane, wid); break;
+    case 2: kloop<kFmt, NFM, 2>(lds0, acc, it, wl, fo, lane, wid); break;
+    case 3: kloop<kFmt, NFM, 3>(lds0, acc, it, wl, fo, lane, wid); break;
+    case 4: kloop<kFmt, NFM, 4>(lds0, acc, it, wl, fo, lane, wid); break;
+    case 5: kloop<kFmt, NFM, 5>(lds0, acc, it, wl, fo, lane, wid); break;
+    case 6: kloop<kFmt, NFM, 6>(lds0, acc, it, wl, fo, lane, wid); break;
+    case 7: kloop<kFmt, NFM, 7>(lds0, acc, it, wl, fo, lane, wid); break;
+    default: kloop<kFmt, NFM, 8>(lds0, acc, it, wl, fo, lane, wid); break;
   }
 }
 
 // kMasked: `psum` is masked_m, `align` is max_m, `status` is unused and the
 // activation rows are the E * max_m slab rows (capacity).
-template <bool kUe8m0, bool kMasked>
+template <int kFmt, bool kMasked>
 __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(
     const uint8_t* __restrict__ a, const uint8_t* __restrict__ a_scale,
     const uint8_t* __restrict__ w, const uint8_t* __restrict__ w_scale,
@@ -577,7 +619,7 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(
   const FragOffsets fo = frag_offsets(lane, wm, wn);
   const uint32_t lds0 = lds_addr(lds);
   const int64_t nrows = kMasked ? capacity : min((int64_t)status[0], capacity);
-  const int sbytes = kUe8m0 ? 1 : 4;
+  const int sbytes = kFmt == kU8 ? 1 : (kFmt == kF32 ? 4 : 0);
   const int KB = K / BK, NT = N / BN;
 
   // Row groups: expert e's block [start_e, end_e) (clamped to the valid rows)
@@ -664,11 +706,11 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(
     wl.init(it, wid, lane, lds0);
     const int role = wid < kLoadWaves ? 0 : it.na;
     switch (nfm) {  // uniform per wave; one K loop per live-tile count and role
-      case 4: kloop_role<kUe8m0, 4>(role, lds0, acc, it, wl, fo, lane, wid); break;
-      case 3: kloop_role<kUe8m0, 3>(role, lds0, acc, it, wl, fo, lane, wid); break;
-      case 2: kloop_role<kUe8m0, 2>(role, lds0, acc, it, wl, fo, lane, wid); break;
-      case 1: kloop_role<kUe8m0, 1>(role, lds0, acc, it, wl, fo, lane, wid); break;
-      default: kloop_role<kUe8m0, 0>(role, lds0, acc, it, wl, fo, lane, wid); break;
+      case 4: kloop_role<kFmt, 4>(role, lds0, acc, it, wl, fo, lane, wid); break;
+      case 3: kloop_role<kFmt, 3>(role, lds0, acc, it, wl, fo, lane, wid); break;
+      case 2: kloop_role<kFmt, 2>(role, lds0, acc, it, wl, fo, lane, wid); break;
+      case 1: kloop_role<kFmt, 1>(role, lds0, acc, it, wl, fo, lane, wid); break;
+      default: kloop_role<kFmt, 0>(role, lds0, acc, it, wl, fo, lane, wid); break;
     }
     wait_lgkm0();
     barrier();  // every wave is done reading the slots
@@ -708,7 +750,9 @@ int device_cus() {
 
 // One workgroup per CU (the kernel uses ~154 KB of LDS), a whole number per
 // XCD, never more than the largest possible number of work items.
-moe_status launch_gemm(bool masked, const void* a, const void* a_scale, moe_scale_fmt fmt,
+// kind: kF32, kU8 or kBF; k is the operand row length in bytes (bf16: 2 per
+// value), so every address in the kernel is a byte offset.
+moe_status launch_gemm(bool masked, const void* a, const void* a_scale, int kind,
                        const void* w, const void* w_scale, const int32_t* psum,
                        const int32_t* status, int64_t capacity, int n, int k, int num_experts,
                        int align, void* out, void* stream) {
@@ -717,10 +761,12 @@ moe_status launch_gemm(bool masked, const void* a, const void* a_scale, moe_scal
   int64_t grid = device_cus();
   if (grid > max_items) grid = max_items;
   grid = (grid + kXcds - 1) / kXcds * kXcds;
-  auto kern = fmt == MOE_SCALE_UE8M0 ? (masked ? grouped_gemm_kernel<true, true>
-                                               : grouped_gemm_kernel<true, false>)
-                                     : (masked ? grouped_gemm_kernel<false, true>
-                                               : grouped_gemm_kernel<false, false>);
+  auto kern = kind == kU8   ? (masked ? grouped_gemm_kernel<kU8, true>
+                                       : grouped_gemm_kernel<kU8, false>)
+              : kind == kBF ? (masked ? grouped_gemm_kernel<kBF, true>
+                                      : grouped_gemm_kernel<kBF, false>)
+                            : (masked ? grouped_gemm_kernel<kF32, true>
+                                      : grouped_gemm_kernel<kF32, false>);
   hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(kThreads), 0, s, (const uint8_t*)a,
                      (const uint8_t*)a_scale, (const uint8_t*)w, (const uint8_t*)w_scale, psum,
                      status, capacity, n, k, num_experts, align, (uint16_t*)out);
@@ -750,7 +796,27 @@ extern "C" moe_status moe_grouped_gemm_fp8(const void* a, const void* a_scale, m
       ((uintptr_t)a_scale % (fmt == MOE_SCALE_F32 ? 16 : 4)) || ((uintptr_t)w_scale % 4))
     return MOE_ERR_ALIGNMENT;
   if (capacity == 0) return MOE_OK;
-  return launch_gemm(false, a, a_scale, fmt, w, w_scale, psum, status, capacity, n, k,
+  return launch_gemm(false, a, a_scale, fmt == MOE_SCALE_UE8M0 ? kU8 : kF32, w, w_scale, psum,
+                     status, capacity, n, k, num_experts, align, out, stream);
+}
+
+extern "C" moe_status moe_grouped_gemm_bf16(const void* a, const void* w, const int32_t* psum,
+                                           const int32_t* status, int64_t capacity, int n,
+                                           int k, int num_experts, int align, void* out,
+                                           void* stream) {
+  if (capacity < 0 || capacity > (1LL << 30) || n <= 0 || k <= 0 || n % BN || k % 64 ||
+      num_experts < 1 || num_experts > MOE_MAX_EXPERTS)
+    return MOE_ERR_SHAPE;
+  if (align < MOE_MIN_ALIGN || align > MOE_MAX_ALIGN || (align & (align - 1)))
+    return MOE_ERR_UNSUPPORTED;
+  if (capacity % align != 0) return MOE_ERR_SHAPE;
+  if (!psum || !status || !w) return MOE_ERR_NULL;
+  if (capacity > 0 && (!a || !out)) return MOE_ERR_NULL;
+  if (2 * k / BK > MAX_KB) return MOE_ERR_UNSUPPORTED;
+  if (((uintptr_t)a % 16) || ((uintptr_t)w % 16) || ((uintptr_t)out % 16))
+    return MOE_ERR_ALIGNMENT;
+  if (capacity == 0) return MOE_OK;
+  return launch_gemm(false, a, nullptr, kBF, w, nullptr, psum, status, capacity, n, 2 * k,
                      num_experts, align, out, stream);
 }
 
@@ -775,6 +841,6 @@ extern "C" moe_status moe_grouped_gemm_fp8_masked(const void* a, const void* a_s
   if (max_m % 16) return MOE_ERR_SHAPE;
   const int64_t rows = (int64_t)max_m * num_experts;
   if (rows == 0) return MOE_OK;
-  return launch_gemm(true, a, a_scale, fmt, w, w_scale, masked_m, nullptr, rows, n, k,
-                     num_experts, max_m, out, stream);
+  return launch_gemm(true, a, a_scale, fmt == MOE_SCALE_UE8M0 ? kU8 : kF32, w, w_scale,
+                     masked_m, nullptr, rows, n, k, num_experts, max_m, out, stream);
 }

@@ -312,7 +312,7 @@ struct RowFetch {
     }
     sf = 0.f;
     sb = 0;
-    if (!kQ && lane < nsc) {
+    if (!kQ && scale_bytes && lane < nsc) {
       if (scale_bytes == 4) sf = reinterpret_cast<const float*>(srow)[lane];
       else sb = srow[lane];
     }
@@ -497,7 +497,7 @@ __global__ __launch_bounds__(kScatterThreads) void expand_scatter_kernel(
   }
   const int total = l_total;
   const int64_t nrows_ex = min((int64_t)total, capacity);
-  const int nsc = hidden / kGroup;
+  const int nsc = scale_bytes ? hidden / kGroup : 0;  // no scales: bf16 rows kept
   const int nch = hidden / 16;                     // 16-byte chunks of an expanded row
   const int nch_in = kQ ? hidden / 8 : nch;        // ... of a received row
 
@@ -643,7 +643,8 @@ extern "C" size_t moe_expand_workspace_bytes(int64_t rows, int topk, int num_exp
 namespace {
 
 // Both entry points.  bf16: x holds bf16 rows, x_stride is in bytes here,
-// x_scale is unused.
+// x_scale is unused; with fmt MOE_SCALE_NONE the rows are kept in bf16 and
+// scattered as 2 * hidden bytes with no scales.
 moe_status expand_layout(bool bf16, const void* x, int64_t x_stride, const void* x_scale,
                          int64_t x_scale_stride, moe_scale_fmt fmt, const int32_t* topk_ids,
                          const float* topk_weights, const int32_t* psum_recv_per_rank,
@@ -659,14 +660,16 @@ moe_status expand_layout(bool bf16, const void* x, int64_t x_stride, const void*
   if (align < MOE_MIN_ALIGN || align > MOE_MAX_ALIGN || (align & (align - 1)))
     return MOE_ERR_UNSUPPORTED;
   if (capacity % align != 0) return MOE_ERR_SHAPE;
-  if (fmt != MOE_SCALE_F32 && fmt != MOE_SCALE_UE8M0) return MOE_ERR_UNSUPPORTED;
+  if (fmt != MOE_SCALE_F32 && fmt != MOE_SCALE_UE8M0 && !(bf16 && fmt == MOE_SCALE_NONE))
+    return MOE_ERR_UNSUPPORTED;
+  const bool keep = fmt == MOE_SCALE_NONE;  // bf16 rows copied as they are
   if (x_stride < (bf16 ? 2 * (int64_t)hidden : hidden) ||
       (!bf16 && x_scale_stride < hidden / kGroup))
     return MOE_ERR_SHAPE;
   if (num_src_ranks < 0 || (psum_recv_per_rank && num_src_ranks == 0)) return MOE_ERR_SHAPE;
   if (!psum || !m_indices || !src2dst || !status) return MOE_ERR_NULL;
   if (rows > 0 && (!x || (!bf16 && !x_scale) || !topk_ids)) return MOE_ERR_NULL;
-  if (capacity > 0 && (!ex || !ex_scale)) return MOE_ERR_NULL;
+  if (capacity > 0 && (!ex || (!keep && !ex_scale))) return MOE_ERR_NULL;
   if (row_weight && !topk_weights && rows > 0) return MOE_ERR_NULL;
   if ((x_stride % 16) || ((uintptr_t)x % 16) || ((uintptr_t)ex % 16)) return MOE_ERR_ALIGNMENT;
   if (!workspace || workspace_bytes_ < workspace_bytes(rows, num_experts))
@@ -677,7 +680,7 @@ moe_status expand_layout(bool bf16, const void* x, int64_t x_stride, const void*
   const int E = num_experts;
   const int64_t ng = num_groups(rows);
   Workspace w = carve(workspace, rows, E);
-  const int scale_bytes = fmt == MOE_SCALE_F32 ? 4 : 1;
+  const int scale_bytes = keep ? 0 : (fmt == MOE_SCALE_F32 ? 4 : 1);
 
   const int G = groups_per_block(E);
   const int64_t nb = num_blocks(rows, E);
@@ -704,15 +707,16 @@ moe_status expand_layout(bool bf16, const void* x, int64_t x_stride, const void*
   if (grid < 1024) grid = 1024;
   if (grid > 16384) grid = 16384;
   const size_t lds = (size_t(4) * E + 1 + (fold ? size_t(nb) * E : 0)) * 4;
-  auto scatter = !bf16 ? expand_scatter_kernel<false, false>
+  auto scatter = !bf16 || keep ? expand_scatter_kernel<false, false>
                  : fmt == MOE_SCALE_UE8M0 ? expand_scatter_kernel<true, true>
                                           : expand_scatter_kernel<true, false>;
   hipLaunchKernelGGL(scatter,
                      dim3((unsigned)grid), dim3(kScatterThreads), lds, s,
                      (const uint8_t*)x, x_stride, (const uint8_t*)x_scale,
                      x_scale_stride * scale_bytes, scale_bytes, topk_ids, topk_weights,
-                     psum_recv_per_rank, num_src_ranks, rows, hidden, topk, E, capacity, align,
-                     w.grp, w.blk, G, (int)nb, w.blk_flag, fold ? 1 : 0, w.starts, w.padbase,
+                     psum_recv_per_rank, num_src_ranks, rows, keep ? 2 * hidden : hidden, topk, E,
+                     capacity, align, w.grp, w.blk, G, (int)nb, w.blk_flag, fold ? 1 : 0,
+                     w.starts, w.padbase,
                      psum, status, (uint8_t*)ex, (uint8_t*)ex_scale, m_indices, src2dst,
                      row_weight);
   if (hipGetLastError() != hipSuccess) return MOE_ERR_LAUNCH;

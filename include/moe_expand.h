@@ -109,7 +109,10 @@ typedef enum {
 
 typedef enum {
   MOE_SCALE_F32 = 0,        /* fp32 scale per group                       */
-  MOE_SCALE_UE8M0 = 1       /* one power-of-two exponent byte per group   */
+  MOE_SCALE_UE8M0 = 1,      /* one power-of-two exponent byte per group   */
+  MOE_SCALE_NONE = 2        /* moe_expand_layout_bf16 only: keep the rows in
+                               bf16, no quantisation, no scales (the bf16-
+                               weight path)                               */
 } moe_scale_fmt;
 
 /* Bits of status[1] written by moe_expand_layout. */
@@ -207,6 +210,9 @@ moe_status moe_expand_layout(
  *                       q = fp8_rne(x * 2^(127-b))
  *              (each operation rounded in fp32; the same rule as
  *              moe_act_quant's).  Rows without a live slot are not read.
+ *              fmt MOE_SCALE_NONE (the bf16-weight path): the rows are kept
+ *              in bf16 and copied as they are; ex is then [capacity, hidden]
+ *              bf16, ex_scale is not used (may be NULL), pad rows are 0.
  * Errors, ownership and every other argument: as moe_expand_layout.
  */
 moe_status moe_expand_layout_bf16(
@@ -325,6 +331,31 @@ moe_status moe_expand_to_masked_slab(
     const void* ex, const void* ex_scale, moe_scale_fmt fmt, const int32_t* psum,
     int32_t* status, int64_t capacity, int hidden, int num_experts, int align, int max_m,
     void* slab, void* slab_scale, int32_t* masked_m, void* stream);
+
+/*
+ * Contiguous grouped bf16 GEMM, "NT" [P3 _run_bf16_contiguous_gemm,
+ * grouped_gemm_nt_bf16_contig]: as moe_grouped_gemm_fp8 with bf16 operands
+ * and no scales.
+ *   a    [capacity, k] bf16, w [num_experts, n, k] bf16 (k contiguous)
+ *   out  [capacity, n] bf16: the fp32 sum of the bf16 products rounded once
+ * Sizes: n % 128 == 0, k % 64 == 0; buffers 16-byte aligned.
+ */
+moe_status moe_grouped_gemm_bf16(
+    const void* a, const void* w, const int32_t* psum, const int32_t* status,
+    int64_t capacity, int n, int k, int num_experts, int align, void* out,
+    void* stream);
+
+/*
+ * SiLU(gate)*up to bf16 for every live expanded row [P3
+ * _run_bf16_contiguous_gemm: silu_and_mul between the bf16 GEMMs]:
+ *   gate_up  [capacity, 2*inter] bf16 -> out [capacity, inter] bf16,
+ *   y = bf16_rne(silu(g) * u) with silu(g) = g / (1 + exp(-g)), in fp32.
+ * Alignment pad rows are not written (the GEMM never reads them).
+ */
+moe_status moe_silu_mul_bf16(
+    const void* gate_up, const int32_t* m_indices, const int32_t* psum,
+    const int32_t* status, int64_t capacity, int inter, int num_experts,
+    int align, void* out, void* stream);
 
 /*
  * Masked grouped fp8 GEMM [P3 _run_masked_gemm]: as moe_grouped_gemm_fp8 on

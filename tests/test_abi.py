@@ -24,6 +24,7 @@ def test_library_exports_every_header_function():
                           "moe_grouped_gemm_fp8", "moe_act_quant",
                           "moe_expand_to_masked_slab", "moe_grouped_gemm_fp8_masked",
                           "moe_act_quant_masked", "moe_masked_slab_to_expand",
+                          "moe_grouped_gemm_bf16", "moe_silu_mul_bf16",
                           "moe_gather", "moe_expand_capacity",
                           "moe_expand_workspace_bytes", "moe_status_string"}
     lib = M.lib()
@@ -209,6 +210,38 @@ def test_masked_entry_points_reject_bad_arguments():
     assert back(mi=None) == M.MOE_ERR_NULL
     assert back(out=MIS) == M.MOE_ERR_ALIGNMENT
     assert back(cap=0) == M.MOE_OK
+
+
+def test_bf16_entry_points_reject_bad_arguments():
+    L = M.lib()
+
+    def gemm(**kw):
+        a = dict(a=FAKE, w=FAKE, psum=FAKE, st=FAKE, cap=320, n=256, k=256, E=4, align=64,
+                 out=FAKE)
+        a.update(kw)
+        return L.moe_grouped_gemm_bf16(a["a"], a["w"], a["psum"], a["st"], a["cap"], a["n"],
+                                       a["k"], a["E"], a["align"], a["out"], None)
+    assert gemm(n=100) == M.MOE_ERR_SHAPE
+    assert gemm(k=96) == M.MOE_ERR_SHAPE
+    assert gemm(cap=100) == M.MOE_ERR_SHAPE
+    assert gemm(align=48) == M.MOE_ERR_UNSUPPORTED
+    assert gemm(psum=None) == M.MOE_ERR_NULL
+    assert gemm(w=MIS) == M.MOE_ERR_ALIGNMENT
+    assert gemm(cap=0) == M.MOE_OK
+
+    def silu(**kw):
+        a = dict(gu=FAKE, mi=FAKE, psum=FAKE, st=FAKE, cap=320, inter=128, E=4, align=64,
+                 out=FAKE)
+        a.update(kw)
+        return L.moe_silu_mul_bf16(a["gu"], a["mi"], a["psum"], a["st"], a["cap"], a["inter"],
+                                   a["E"], a["align"], a["out"], None)
+    assert silu(inter=100) == M.MOE_ERR_SHAPE
+    assert silu(st=None) == M.MOE_ERR_NULL
+    assert silu(out=MIS) == M.MOE_ERR_ALIGNMENT
+    assert silu(cap=0) == M.MOE_OK
+    # keep-bf16 layout: ex_scale may be NULL, the plain layout refuses the format
+    assert _layout_bf16(fmt=2, exs=None, wsb=16) == M.MOE_ERR_WORKSPACE
+    assert _layout(fmt=2) == M.MOE_ERR_UNSUPPORTED
 
 
 def test_gather_rejects_bad_arguments():
