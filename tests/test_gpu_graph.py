@@ -13,7 +13,6 @@ no memset nodes (it clears nothing with hipMemsetAsync), and the tests
 capture nothing but its launches.
 """
 
-import numpy as np
 import pytest
 
 torch = pytest.importorskip("torch")
@@ -27,21 +26,25 @@ if not torch.cuda.is_available():
     pytest.skip("needs a GPU", allow_module_level=True)
 
 
-def _replay_check(mod, call, inputs_a, inputs_b, out):
-    """Capture call() on the buffers in inputs_a; replay with a and b in turn
-    (copied into those buffers) and compare each replay with an eager run."""
-    bufs = inputs_a
-    eager = {}
-    for name, src in (("a", inputs_a), ("b", inputs_b)):
+def _replay_check(mod, call, bufs, inputs_a, inputs_b, out):
+    """call() reads its inputs from `bufs`.  Run it eagerly on a and on b
+    (copied into bufs), capture it, then replay with a, b, a copied into the
+    same buffers, each replay compared with the eager run on those inputs.
+    The output is refilled with the same value before every run (rows past
+    the valid boundary are never written)."""
+    def load(src):
         for k in bufs:
             if bufs[k] is not None:
                 bufs[k].copy_(src[k])
+
+    eager = {}
+    for name, src in (("a", inputs_a), ("b", inputs_b)):
+        load(src)
+        out.fill_(-3.0)
         call()
         torch.cuda.synchronize()
         eager[name] = out.clone()
-    for k in bufs:
-        if bufs[k] is not None:
-            bufs[k].copy_(inputs_a[k])
+    load(inputs_a)
     s = torch.cuda.Stream()
     s.wait_stream(torch.cuda.current_stream())
     g = torch.cuda.CUDAGraph()
@@ -53,10 +56,7 @@ def _replay_check(mod, call, inputs_a, inputs_b, out):
     torch.cuda.current_stream().wait_stream(s)
     torch.cuda.synchronize()
     for rep, name in enumerate(("a", "b", "a")):
-        src = inputs_a if name == "a" else inputs_b
-        for k in bufs:
-            if bufs[k] is not None:
-                bufs[k].copy_(src[k])
+        load(inputs_a if name == "a" else inputs_b)
         out.fill_(-3.0)            # eager work between replays
         torch.cuda.synchronize()
         g.replay()
@@ -76,12 +76,14 @@ def test_expand_path_graph_replay(fmt):
     mod = M.ExpandedMoE(R, T, ga["w13"], ga["w13_scale"], ga["w2"], ga["w2_scale"],
                         a["align"], fmt)
     out = torch.zeros((R, mod.H), dtype=torch.bfloat16, device="cuda")
-    ins_a = {k: ga[k].clone() for k in ("x", "x_scale", "ids", "w", "prank")}
-    ins_b = {k: gb[k] for k in ins_a}
+    keys = ("x", "x_scale", "ids", "w", "prank")
+    bufs = {k: ga[k].clone() for k in keys}
+    ins_a = {k: ga[k] for k in keys}
+    ins_b = {k: gb[k] for k in keys}
 
     def call():
-        mod(ins_a["x"], ins_a["x_scale"], ins_a["ids"], ins_a["w"], ins_a["prank"], out=out)
-    _replay_check(mod, call, ins_a, ins_b, out)
+        mod(bufs["x"], bufs["x_scale"], bufs["ids"], bufs["w"], bufs["prank"], out=out)
+    _replay_check(mod, call, bufs, ins_a, ins_b, out)
 
 
 def test_masked_decode_path_graph_replay():
@@ -92,9 +94,11 @@ def test_masked_decode_path_graph_replay():
     mod = M.MaskedMoE(R, T, ga["w13"], ga["w13_scale"], ga["w2"], ga["w2_scale"], a["align"],
                       64, a["fmt"])
     out = torch.zeros((R, mod.H), dtype=torch.bfloat16, device="cuda")
-    ins_a = {k: ga[k].clone() for k in ("x", "x_scale", "ids", "w")}
-    ins_b = {k: gb[k] for k in ins_a}
+    keys = ("x", "x_scale", "ids", "w")
+    bufs = {k: ga[k].clone() for k in keys}
+    ins_a = {k: ga[k] for k in keys}
+    ins_b = {k: gb[k] for k in keys}
 
     def call():
-        mod(ins_a["x"], ins_a["x_scale"], ins_a["ids"], ins_a["w"], None, out=out)
-    _replay_check(mod, call, ins_a, ins_b, out)
+        mod(bufs["x"], bufs["x_scale"], bufs["ids"], bufs["w"], None, out=out)
+    _replay_check(mod, call, bufs, ins_a, ins_b, out)
