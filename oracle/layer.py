@@ -124,7 +124,7 @@ def act_quant(G, live, fmt: str, fold_weight=None):
     n, two_i = G.shape
     inter = two_i // 2
     q = np.zeros((n, inter), dtype=np.uint8)
-    s = np.zeros((n, inter // quant.GROUP),
+    s = np.zeros((n, inter // (quant.MX_GROUP if fmt == "mxfp8" else quant.GROUP)),
                  dtype=np.float32 if fmt == "f32" else np.uint8)
     rows = np.nonzero(live)[0]
     if len(rows):

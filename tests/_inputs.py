@@ -15,8 +15,9 @@ def quantise(data, fmt=None):
     fmt = fmt or wl.fmt
     R, H = data["x"].shape
     sdt = np.float32 if fmt == "f32" else np.uint8
+    g = 32 if fmt == "mxfp8" else 128
     x_q = np.empty((R, H), np.uint8)
-    x_s = np.empty((R, H // 128), sdt)
+    x_s = np.empty((R, H // g), sdt)
     for r0 in range(0, R, 2048):
         x_q[r0:r0 + 2048], x_s[r0:r0 + 2048] = quant.quantize_rows(data["x"][r0:r0 + 2048], fmt)
     W.poison_tail(data, x_q, x_s)
@@ -24,7 +25,7 @@ def quantise(data, fmt=None):
     def blocks(w):
         E, N, K = w.shape
         q = np.empty((E, N, K), np.uint8)
-        s = np.empty((E, N // 128, K // 128), sdt)
+        s = np.empty((E, N, K // 32) if fmt == "mxfp8" else (E, N // 128, K // 128), sdt)
         for e in range(E):
             q[e:e + 1], s[e:e + 1] = quant.quantize_blocks(w[e:e + 1], fmt)
         return q, s
