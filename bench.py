@@ -47,10 +47,12 @@ def parse():
 
 
 def quant_rows(x, fmt):
-    """[R, H] fp32 -> fp8 codes (uint8 view) and per-1x128 scales."""
+    """[R, H] fp32 -> fp8 codes (uint8 view) and per-1x128 scales (MXFP8:
+    per-1x32 UE8M0 bytes)."""
     import torch
     R, H = x.shape
-    g = x.view(R, H // 128, 128)
+    gs = 32 if fmt == "mxfp8" else 128
+    g = x.view(R, H // gs, gs)
     amax = g.abs().amax(-1, keepdim=True).clamp_min(1e-10)
     if fmt == "f32":
         q = (g * (448.0 / amax)).to(torch.float8_e4m3fn)
@@ -59,7 +61,7 @@ def quant_rows(x, fmt):
         m, e = torch.frexp(amax / 448.0)
         e = torch.where(m == 0.5, e - 1, e)                  # ceil(log2)
         q = torch.ldexp(g, (-e).float()).to(torch.float8_e4m3fn)
-        s = (e + 127).to(torch.uint8).view(R, H // 128)
+        s = (e + 127).to(torch.uint8).view(R, H // gs)
     return q.view(R, H).view(torch.uint8).contiguous(), s.contiguous()
 
 
@@ -67,6 +69,9 @@ def quant_blocks(w, fmt):
     """[E, N, K] fp32 -> fp8 codes and per-128x128 scales."""
     import torch
     E, N, K = w.shape
+    if fmt == "mxfp8":       # one UE8M0 byte per 1x32 group of every row
+        q, s = quant_rows(w.reshape(E * N, K), "mxfp8")
+        return q.view(E, N, K), s.view(E, N, K // 32)
     t = w.view(E, N // 128, 128, K // 128, 128)
     amax = t.abs().amax(dim=(2, 4), keepdim=True).clamp_min(1e-10)
     if fmt == "f32":
@@ -86,10 +91,13 @@ def make_weights(wl, device, gen):
     import torch
     E, H, I = wl.experts, wl.hidden, wl.inter
     sdt = torch.float32 if wl.fmt == "f32" else torch.uint8
+    mx = wl.fmt == "mxfp8"
     w13q = torch.empty((E, 2 * I, H), dtype=torch.uint8, device=device)
-    w13s = torch.empty((E, 2 * I // 128, H // 128), dtype=sdt, device=device)
+    w13s = torch.empty((E, 2 * I, H // 32) if mx else (E, 2 * I // 128, H // 128), dtype=sdt,
+                       device=device)
     w2q = torch.empty((E, H, I), dtype=torch.uint8, device=device)
-    w2s = torch.empty((E, H // 128, I // 128), dtype=sdt, device=device)
+    w2s = torch.empty((E, H, I // 32) if mx else (E, H // 128, I // 128), dtype=sdt,
+                      device=device)
     step = 16
     for e0 in range(0, E, step):
         e1 = min(E, e0 + step)
@@ -184,12 +192,13 @@ def measured_traffic(workload):
     return int(rec["traffic_bytes_per_launch"])
 
 
-def gemm_cost(rows, n, k, nonempty, sbytes, eb=1):
+def gemm_cost(rows, n, k, nonempty, sbytes, eb=1, mx=False):
     """Algorithmic HBM bytes and useful flops of one grouped GEMM launch: each
     non-empty expert's weights and block scales once, the live rows'
     activations and scales once, their bf16 outputs once (eb: bytes per
     operand value, 1 for fp8, 2 for bf16)."""
-    weights = nonempty * (n * k * eb + (n // 128) * (k // 128) * sbytes)
+    wsc = n * (k // 32) if mx else (n // 128) * (k // 128) * sbytes   # MXFP8: per row, 1x32
+    weights = nonempty * (n * k * eb + wsc)
     acts = rows * (k * eb + (k // 128) * sbytes)
     return weights + acts + rows * n * 2, 2.0 * rows * n * k
 
@@ -386,13 +395,14 @@ def main():
     m_used = int(status[0])
     nonempty = int((counts > 0).sum())
     H, I = wl.hidden, wl.inter
-    sb = 0 if wbf else (4 if wl.fmt == "f32" else 1)
+    mx = wl.fmt == "mxfp8"
+    sb = 0 if wbf else (4 if wl.fmt in ("f32", "mxfp8") else 1)   # scale bytes per 128 values
     eb = 2 if wbf else 1
     peak_tf = BF16_PEAK_TFLOPS if wbf else FP8_PEAK_TFLOPS
     # Dominant kernel: the grouped GEMM, averaged over its two launches per
     # step (gate_up [A, 2I] x K=H, then down [A, H] x K=I; A = live rows).
-    g1_bytes, g1_flops = gemm_cost(A, 2 * I, H, nonempty, sb, eb)
-    g2_bytes, g2_flops = gemm_cost(A, H, I, nonempty, sb, eb)
+    g1_bytes, g1_flops = gemm_cost(A, 2 * I, H, nonempty, sb, eb, mx)
+    g2_bytes, g2_flops = gemm_cost(A, H, I, nonempty, sb, eb, mx)
     t = (gemm1_us + gemm2_us) * 1e-6
     byts, flops = g1_bytes + g2_bytes, g1_flops + g2_flops
     if byts / (HBM_PEAK_GBS * 1e9) >= flops / (peak_tf * 1e12):
@@ -403,7 +413,7 @@ def main():
                 "unit": "TFLOP/s"}
     roof["frac"] = roof["achieved"] / roof["peak"]
     roof["traffic"] = measured_traffic(wl.name)
-    roof["kernel"] = (f"grouped_gemm_kernel<{'bf16' if wbf else ('ue8m0' if wl.fmt == 'ue8m0' else 'fp32-scale fp8')}, "
+    roof["kernel"] = (f"grouped_gemm_kernel<{'bf16' if wbf else {'ue8m0': 'ue8m0', 'mxfp8': 'mxfp8'}.get(wl.fmt, 'fp32-scale fp8')}, "
                       f"{'masked' if masked else 'contiguous'}> "
                       "(mean over its gate_up and down launches)")
     roof["launch_us"] = {"gate_up": gemm1_us, "down": gemm2_us, "mean": (gemm1_us + gemm2_us) / 2}

@@ -31,9 +31,10 @@ HEADER_PATH = os.path.join(os.path.dirname(_HERE), "include", "moe_expand.h")
 
 MOE_OK, MOE_ERR_NULL, MOE_ERR_SHAPE, MOE_ERR_ALIGNMENT = 0, 1, 2, 3
 MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE, MOE_ERR_LAUNCH = 4, 5, 6
-MOE_SCALE_F32, MOE_SCALE_UE8M0, MOE_SCALE_NONE = 0, 1, 2
+MOE_SCALE_F32, MOE_SCALE_UE8M0, MOE_SCALE_NONE, MOE_SCALE_MXFP8 = 0, 1, 2, 3
 MOE_FLAG_CAPACITY_OVERFLOW, MOE_FLAG_EXPERT_ID_RANGE, MOE_FLAG_SLAB_OVERFLOW = 1, 2, 4
-FMT = {"f32": MOE_SCALE_F32, "ue8m0": MOE_SCALE_UE8M0, "none": MOE_SCALE_NONE}
+FMT = {"f32": MOE_SCALE_F32, "ue8m0": MOE_SCALE_UE8M0, "none": MOE_SCALE_NONE,
+       "mxfp8": MOE_SCALE_MXFP8}
 
 _P = ctypes.c_void_p
 _I64 = ctypes.c_int64
@@ -262,7 +263,8 @@ class ExpandedMoE:
     Weights: w13 [E, 2I, H] fp8 + w13_scale [E, 2I/128, H/128];
     w2 [E, H, I] fp8 + w2_scale [E, H/128, I/128] (fp32 or UE8M0 bytes).
     Scale format 'f32' folds the top-k weight into the down GEMM's input
-    scale; 'ue8m0' weights the down output in the gather."""
+    scale; 'ue8m0' and 'mxfp8' (1x32 UE8M0 groups, weight scales [E, N,
+    K/32]) weight the down output in the gather."""
 
     def __init__(self, rows, topk, w13, w13_scale, w2, w2_scale, align, fmt="f32",
                  device="cuda"):
@@ -275,7 +277,9 @@ class ExpandedMoE:
         self.rows, self.topk = rows, topk
         cap = moe_expand_capacity(rows, topk, E, align)
         self.capacity = cap
-        sdt = torch.float32 if fmt == "f32" else torch.uint8
+        # expanded scales: fp32 or UE8M0 bytes per (128-wide block, row); MXFP8
+        # one 4-byte word (the block's four 1x32 bytes) per (block, row)
+        sdt = {"f32": torch.float32, "ue8m0": torch.uint8, "mxfp8": torch.int32}[fmt]
         dev = device
         u8 = torch.uint8
         self.ex = torch.empty((cap, H), dtype=u8, device=dev)

@@ -33,7 +33,9 @@ __device__ __forceinline__ float silu_mul(float g, float u) {
 // _run_bf16_contiguous_gemm: silu_and_mul to bf16 between the bf16 GEMMs):
 // y is rounded to bf16 and stored to `out` as [capacity, inter] bf16, with no
 // quantisation; pad rows are not written (the GEMM never reads them).
-template <bool kUe8m0, bool kFold, bool kMasked, bool kBfOut = false>
+// kMx (MXFP8, with kUe8m0): 1x32 groups (4 lanes), each group's UE8M0 byte
+// stored as byte (col / 32) % 4 of the row's word for its 128-wide block.
+template <bool kUe8m0, bool kFold, bool kMasked, bool kBfOut = false, bool kMx = false>
 __global__ __launch_bounds__(kThreads) void act_quant_kernel(
     const uint16_t* __restrict__ gu, const int32_t* __restrict__ m_indices,
     const int32_t* __restrict__ psum, const int32_t* __restrict__ status, int64_t capacity,
@@ -94,7 +96,8 @@ __global__ __launch_bounds__(kThreads) void act_quant_kernel(
       for (int c = t; c < inter / 16; c += kThreads)
         reinterpret_cast<u32x4*>(qrow)[c] = u32x4{0u, 0u, 0u, 0u};
       for (int g = t; g < ngroups; g += kThreads) {
-        if (kUe8m0) out_scale[g * capacity + m] = 0;
+        if (kMx) reinterpret_cast<uint32_t*>(out_scale)[g * capacity + m] = 0u;
+        else if (kUe8m0) out_scale[g * capacity + m] = 0;
         else reinterpret_cast<float*>(out_scale)[g * capacity + m] = 0.f;
       }
       continue;
@@ -119,7 +122,7 @@ __global__ __launch_bounds__(kThreads) void act_quant_kernel(
         for (int i = 0; i < 8; ++i) amax = fmaxf(amax, fabsf(y[i]));
       }
 #pragma unroll
-      for (int o = 8; o > 0; o >>= 1) amax = fmaxf(amax, __shfl_xor(amax, o, 64));
+      for (int o = kMx ? 2 : 8; o > 0; o >>= 1) amax = fmaxf(amax, __shfl_xor(amax, o, 64));
       amax = fmaxf(amax, 1e-10f);
       if (!active) continue;
       float scale_out = 0.f;
@@ -141,7 +144,11 @@ __global__ __launch_bounds__(kThreads) void act_quant_kernel(
       int hi = __builtin_amdgcn_cvt_pk_fp8_f32(p[4], p[5], 0, false);
       hi = __builtin_amdgcn_cvt_pk_fp8_f32(p[6], p[7], hi, true);
       *reinterpret_cast<uint2*>(qrow + col) = make_uint2((uint32_t)lo, (uint32_t)hi);
-      if ((lane & 15) == 0) {
+      if constexpr (kMx) {
+        if ((lane & 3) == 0)
+          out_scale[((int64_t)(col / kGroup) * capacity + m) * 4 + (col / 32) % 4] =
+              (uint8_t)sbyte;
+      } else if ((lane & 15) == 0) {
         const int grp = col / kGroup;
         if (kUe8m0) out_scale[grp * capacity + m] = (uint8_t)sbyte;
         else reinterpret_cast<float*>(out_scale)[grp * capacity + m] = scale_out;
@@ -166,15 +173,18 @@ extern "C" moe_status moe_act_quant(const void* gate_up, const int32_t* m_indice
   if (align < MOE_MIN_ALIGN || align > MOE_MAX_ALIGN || (align & (align - 1)))
     return MOE_ERR_UNSUPPORTED;
   if (capacity % align != 0) return MOE_ERR_SHAPE;
-  if (fmt != MOE_SCALE_F32 && fmt != MOE_SCALE_UE8M0) return MOE_ERR_UNSUPPORTED;
-  if (fmt == MOE_SCALE_UE8M0 && fold_weight) return MOE_ERR_UNSUPPORTED;
+  if (fmt != MOE_SCALE_F32 && fmt != MOE_SCALE_UE8M0 && fmt != MOE_SCALE_MXFP8)
+    return MOE_ERR_UNSUPPORTED;
+  if (fmt != MOE_SCALE_F32 && fold_weight) return MOE_ERR_UNSUPPORTED;
   if (!m_indices || !psum || !status) return MOE_ERR_NULL;
   if (capacity > 0 && (!gate_up || !out || !out_scale)) return MOE_ERR_NULL;
   if (((uintptr_t)gate_up % 16) || ((uintptr_t)out % 16)) return MOE_ERR_ALIGNMENT;
+  if (fmt != MOE_SCALE_UE8M0 && ((uintptr_t)out_scale % 4)) return MOE_ERR_ALIGNMENT;
   if (capacity == 0) return MOE_OK;
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   int64_t grid = capacity < 2048 ? capacity : 2048;  // grid-stride over the live rows
-  auto kern = fmt == MOE_SCALE_UE8M0 ? act_quant_kernel<true, false, false>
+  auto kern = fmt == MOE_SCALE_MXFP8 ? act_quant_kernel<true, false, false, false, true>
+              : fmt == MOE_SCALE_UE8M0 ? act_quant_kernel<true, false, false>
               : fold_weight           ? act_quant_kernel<false, true, false>
                                       : act_quant_kernel<false, false, false>;
   hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(kThreads), 0, s, (const uint16_t*)gate_up,

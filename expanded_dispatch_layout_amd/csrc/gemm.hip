@@ -59,8 +59,12 @@ typedef int v8i __attribute__((ext_vector_type(8)));
 typedef float v4f __attribute__((ext_vector_type(4)));
 
 // Operand formats: fp8 with fp32 scales (promoted in VALU), fp8 with UE8M0
-// scales (the MFMA's own scale operands), bf16 (no scales).
-constexpr int kF32 = 0, kU8 = 1, kBF = 2;
+// scales (the MFMA's own scale operands), bf16 (no scales), MXFP8 (a UE8M0
+// byte per 1x32 group of every activation row and every weight row: each
+// lane passes the bytes of its own rows' 32-wide K chunk).
+constexpr int kF32 = 0, kU8 = 1, kBF = 2, kMX = 3;
+constexpr int kMxMaxExperts = 256;  // MXFP8: smaller expert tables make room for
+constexpr int WSC_SLOT = 1024;      // the weight-scale ring (4 waves x 256 B per slot)
 
 constexpr int kThreads = 512;  // 8 waves: 2 per SIMD
 constexpr int kWaves = kThreads / 64;
@@ -205,7 +209,9 @@ struct Item {
                         // rest of the group is alignment padding
   int KB;               // K / 128
   int K;
-  int sbytes;           // 4 (fp32) or 1 (UE8M0)
+  int sbytes;           // 4 (fp32, MXFP8 words) or 1 (UE8M0)
+  const uint8_t* ws;    // MXFP8: scales of the N tile's first weight row (K/32 bytes per row)
+  uint32_t wsc_lds;     // MXFP8: LDS address of the weight-scale ring
   int blocks;           // 8-row blocks holding live rows
   int na;               // blocks per activation-loading wave per stage (1..8)
   int a_slot_bytes;     // activation slot: 32 * na rows x 128 B
@@ -253,12 +259,14 @@ struct WaveLoads {
   uint32_t off[A_LOADS];  // weights use the first B_LOADS
   int lds_off[A_LOADS];
   uint32_t scale_off;     // source offset of this lane's scale word
+  uint32_t wsc_off;       // MXFP8 weight waves: offset of weight row w * 32 + lane % 32's scales
   uint32_t scale_rel;     // its LDS offset within the scale slot
   uint32_t dummy;         // LDS address of this wave's dummy area (0: none)
 
   __device__ __forceinline__ void init(const Item& it, int wid, int lane, uint32_t lds0) {
     const bool wload = wid < kLoadWaves;
     const int w = wload ? wid : wid - kLoadWaves;
+    wsc_off = (uint32_t)(w * 32 + (lane & 31)) * (uint32_t)(it.K / 32);
     const int nreal = wload ? B_LOADS : max(0, min(it.na, (it.blocks - w + kLoadWaves - 1) / kLoadWaves));
 #pragma unroll
     for (int j = 0; j < A_LOADS; ++j) {
@@ -299,6 +307,8 @@ struct WaveLoads {
 // i * A_TILE_STRIDE, column tile j adds j * 2048.
 struct FragOffsets {
   int a_lo, a_hi, b_lo, b_hi, m_row;
+  int wsc_lane;  // MXFP8: this lane's weight row's word in a weight-scale slot (column tile 0)
+  int a_mx[4], b_mx[4];  // MXFP8: the four 8-byte pieces of this lane's fragments
 };
 
 __device__ __forceinline__ FragOffsets frag_offsets(int lane, int wm, int wn) {
@@ -310,7 +320,36 @@ __device__ __forceinline__ FragOffsets frag_offsets(int lane, int wm, int wn) {
   f.b_lo = swz(rb, fk);  // within a weight slot
   f.b_hi = swz(rb, fk + 1);
   f.m_row = wm * 16 + frow;  // this lane's output row in row tile 0
+  // Weight row r = wn * 64 + frow + 16 j sits at (r / 32) * 256 + (r % 32) * 4
+  // of a slot: this lane's base plus (j / 2) * 256 + (j % 2) * 64.
+  f.wsc_lane = wn * 512 + frow * 4;
+  // MXFP8: with a scale per 32-wide K block the order of K inside a lane
+  // matters (with one scale per row, as in the other formats, only the
+  // pairing of A and B does).  The scaled MFMA takes a lane's 32 bytes as two
+  // 16-byte halves, K [16 g, 16 g + 16) and [64 + 16 g, 64 + 16 g + 16) for
+  // lane group g = lane / 16, with lane l's scale register scaling block g of
+  // its row (measured on gfx950 with per-block scales on either operand,
+  // against the two other plausible orders).  So lane l brings logical
+  // 16-byte chunks g and 4 + g.
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const int c = (lane >> 4) + 4 * (q >> 1), h = (q & 1) * 8;
+    f.a_mx[q] = swz(ra, c) + h;
+    f.b_mx[q] = swz(rb, c) + h;
+  }
   return f;
+}
+
+typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ v8i frag4x8(uint32_t base, const int (&off)[4]) {
+  v8i r;
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const u32x2 p = lds_load<u32x2>(base + off[q]);
+    r[2 * q] = (int)p[0];
+    r[2 * q + 1] = (int)p[1];
+  }
+  return r;
 }
 
 __device__ __forceinline__ v8i frag2(uint32_t base, int lo_off, int hi_off) {
@@ -363,6 +402,28 @@ struct StepScales<kF32, NFM> {
   }
 };
 template <int NFM>
+struct StepScales<kMX, NFM> {  // MXFP8: per-lane bytes of its rows' 32-wide K chunk
+  int abyte[NFM];  // this lane's activation row, per row tile
+  int sbyte[FN];   // this lane's weight row, per column tile
+  // Step kb's bytes, read straight into the registers its MFMAs take: lane l
+  // holds K chunk l / 16 of the step, which is byte l / 16 of its rows'
+  // words.  Issued after the step before has issued its last MFMA; the LDS
+  // wait before the next barrier covers them (only one step's bytes live).
+  __device__ __forceinline__ void load(uint32_t sc, const Item& it, const FragOffsets& fo,
+                                       int kb, int lane) {
+    const uint32_t ws = it.wsc_lds + (uint32_t)(kb % kBSlots) * WSC_SLOT + (lane >> 4);
+#pragma unroll
+    for (int j = 0; j < FN; ++j)
+      sbyte[j] = lds_load<uint8_t>(ws + fo.wsc_lane + (j >> 1) * 256 + (j & 1) * 64);
+#pragma unroll
+    for (int i = 0; i < NFM; ++i)
+      abyte[i] = lds_load<uint8_t>(sc + (fo.m_row + i * ROW_TILE_STRIDE) * 4 + (lane >> 4));
+  }
+  __device__ __forceinline__ void read(uint32_t, uint32_t, const Item&, const FragOffsets&, int,
+                                       int) {}
+  __device__ __forceinline__ void finish(const Item&, const FragOffsets&, int, int) {}
+};
+template <int NFM>
 struct StepScales<kU8, NFM> {
   uint32_t raw[NFM];  // row r's exponent byte is byte r of the slot
   uint32_t wraw;
@@ -405,8 +466,13 @@ __device__ __forceinline__ void step(v8i (&a)[FM], v8i (&b)[FN], v4f (&acc)[FM][
   auto refresh = [&](int t) __attribute__((always_inline)) {  // after MFMA t
     if constexpr (kNext) {
       const int i = t / FN, j = t % FN;
-      if (i == NFM - 1) b[j] = frag2(next_b + j * 2048, fo.b_lo, fo.b_hi);
-      if (j == FN - 1) a[i] = frag2(next_a + i * A_TILE_STRIDE, fo.a_lo, fo.a_hi);
+      if constexpr (kFmt == kMX) {
+        if (i == NFM - 1) b[j] = frag4x8(next_b + j * 2048, fo.b_mx);
+        if (j == FN - 1) a[i] = frag4x8(next_a + i * A_TILE_STRIDE, fo.a_mx);
+      } else {
+        if (i == NFM - 1) b[j] = frag2(next_b + j * 2048, fo.b_lo, fo.b_hi);
+        if (j == FN - 1) a[i] = frag2(next_a + i * A_TILE_STRIDE, fo.a_lo, fo.a_hi);
+      }
     }
   };
   auto side = [&](int t) __attribute__((always_inline)) {  // after MFMA t: work not feeding this step
@@ -416,6 +482,8 @@ __device__ __forceinline__ void step(v8i (&a)[FM], v8i (&b)[FN], v4f (&acc)[FM][
     }
     if constexpr (kFmt == kU8 && kNext)
       if (t == M - 1) ss.finish(it, fo, kb + 1, lane);       // the next step's operands
+    if constexpr (kFmt == kMX && kNext)
+      if (t == M - 1) ss.load(next_sc, it, fo, kb + 1, lane);  // after the last MFMA
     if (t == (M > 1 ? 1 : 0)) issue();
   };
   if constexpr (kFmt == kBF) {
@@ -448,13 +516,16 @@ __device__ __forceinline__ void step(v8i (&a)[FM], v8i (&b)[FN], v4f (&acc)[FM][
       refresh(t);
       sched_fence();
     }
-  } else if constexpr (kFmt == kU8) {
+  } else if constexpr (kFmt == kU8 || kFmt == kMX) {
     // The exponent bytes are the MFMA's own scale operands.
 #pragma unroll
     for (int t = 0; t < M; ++t) {
       const int i = t / FN, j = t % FN;
+      int sb;
+      if constexpr (kFmt == kMX) sb = ss.sbyte[j];
+      else sb = ss.sbyte;
       acc[i][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(b[j], a[i], acc[i][j], 0, 0, 0,
-                                                                   ss.sbyte, 0, ss.abyte[i]);
+                                                                   sb, 0, ss.abyte[i]);
       sched_fence();
       side(t);
       refresh(t);
@@ -503,7 +574,8 @@ __device__ __forceinline__ void kloop(uint32_t lds0, v4f (&acc)[FM][FN], const I
                                       int wid) {
   constexpr bool kW = ROLE == 0;
   constexpr bool kSc = kFmt != kBF;                   // activation scales streamed
-  constexpr int NL = kW ? W_LOADS : ROLE + (kSc ? 1 : 0);  // loads per stage
+  constexpr bool kMxW = kW && kFmt == kMX;            // + the weight rows' scale words
+  constexpr int NL = kW ? W_LOADS + (kMxW ? 1 : 0) : ROLE + (kSc ? 1 : 0);  // loads per stage
   constexpr int D = kW ? kBSlots : act_slots(ROLE);   // stream depth (slots)
   const int KB = it.KB;
   const uint32_t a_end = lds0 + A_BASE + (uint32_t)(it.na_slots * it.a_slot_bytes);
@@ -512,10 +584,21 @@ __device__ __forceinline__ void kloop(uint32_t lds0, v4f (&acc)[FM][FN], const I
   const uint8_t* src = uniform_ptr(kW ? it.b : it.a);
   const uint8_t* ssrc = uniform_ptr(it.as);
   uint32_t dst = kW ? lds0 : lds0 + A_BASE, sdst = lds0 + SC_BASE;
+  // MXFP8 weight waves: wave wid brings weight rows wid * 32 .. + 31's scale
+  // words of each stage (lanes 32-63 repeat lanes 0-31 into the upper half of
+  // its 256 bytes) into the slot that matches the weight slot.
+  const uint8_t* wsrc = kMxW ? uniform_ptr(it.ws) : nullptr;
+  const uint32_t wbase = kMxW ? it.wsc_lds + (uint32_t)wid * 256u : 0u;
+  uint32_t wdst = wbase;
   auto issue = [&]() __attribute__((always_inline)) {
     if constexpr (kW) {
       wl.weights(src, dst);
       dst = dst + B_BYTES == lds0 + B_RING ? lds0 : dst + B_BYTES;
+      if constexpr (kMxW) {
+        dma4(wsrc, wl.wsc_off, wdst);
+        wsrc += 4;
+        wdst = wdst + WSC_SLOT == wbase + kBSlots * WSC_SLOT ? wbase : wdst + WSC_SLOT;
+      }
     } else {
       wl.template acts<ROLE, kSc>(src, dst, ssrc, sdst);
       dst = dst + it.a_slot_bytes == a_end ? lds0 + A_BASE : dst + it.a_slot_bytes;
@@ -531,7 +614,7 @@ __device__ __forceinline__ void kloop(uint32_t lds0, v4f (&acc)[FM][FN], const I
 
   // The item's weight block scales: issued before this wave's stage 0, so
   // the prologue's wait for stage 0 covers them too (loads complete in order).
-  if constexpr (kSc)
+  if constexpr (kSc && kFmt != kMX)
     if (wid == kWaves - 1) load_item_wscales(it, lds0, lane);
   // Prologue: stages 0..D-2 of the stream, wait for stage 0 with the rest
   // in flight; after the barrier, read stage 0's fragments and issue the
@@ -544,12 +627,21 @@ __device__ __forceinline__ void kloop(uint32_t lds0, v4f (&acc)[FM][FN], const I
   StepScales<kFmt, NFM> ss;
   if constexpr (NFM > 0) {
 #pragma unroll
-    for (int j = 0; j < FN; ++j) b[j] = frag2(lds0 + j * 2048, fo.b_lo, fo.b_hi);
+    for (int j = 0; j < FN; ++j) {
+      if constexpr (kFmt == kMX) b[j] = frag4x8(lds0 + j * 2048, fo.b_mx);
+      else b[j] = frag2(lds0 + j * 2048, fo.b_lo, fo.b_hi);
+    }
 #pragma unroll
-    for (int i = 0; i < NFM; ++i)
-      a[i] = frag2(lds0 + A_BASE + i * A_TILE_STRIDE, fo.a_lo, fo.a_hi);
-    ss.read(lds0 + SC_BASE, bsc, it, fo, 0, lane);
-    if constexpr (kFmt == kU8) ss.finish(it, fo, 0, lane);
+    for (int i = 0; i < NFM; ++i) {
+      if constexpr (kFmt == kMX) a[i] = frag4x8(lds0 + A_BASE + i * A_TILE_STRIDE, fo.a_mx);
+      else a[i] = frag2(lds0 + A_BASE + i * A_TILE_STRIDE, fo.a_lo, fo.a_hi);
+    }
+    if constexpr (kFmt == kMX) {
+      ss.load(lds0 + SC_BASE, it, fo, 0, lane);
+    } else {
+      ss.read(lds0 + SC_BASE, bsc, it, fo, 0, lane);
+      if constexpr (kFmt == kU8) ss.finish(it, fo, 0, lane);
+    }
   }
   if (pre < KB) issue();  // stages 0 .. min(D, KB) - 1 are now in flight
   // Read-side slot of stage kb+1's scales.
@@ -610,16 +702,18 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(
     const uint8_t* __restrict__ w, const uint8_t* __restrict__ w_scale,
     const int32_t* __restrict__ psum, const int32_t* __restrict__ status, int64_t capacity, int N,
     int K, int E, int align, uint16_t* __restrict__ out) {
+  constexpr int kMaxE = kFmt == kMX ? kMxMaxExperts : MOE_MAX_EXPERTS;
   __shared__ __attribute__((aligned(16))) uint8_t lds[LDS_BYTES];
-  __shared__ int gp[MOE_MAX_EXPERTS + 1];  // prefix of row groups per expert
-  __shared__ int pe[MOE_MAX_EXPERTS];      // end of each expert's live rows
+  __shared__ int gp[kMaxE + 1];  // prefix of row groups per expert
+  __shared__ int pe[kMaxE];      // end of each expert's live rows
+  __shared__ __attribute__((aligned(16))) uint8_t wsc[kFmt == kMX ? kBSlots * WSC_SLOT : 16];
   const int t = threadIdx.x, lane = t & 63;
   const int wid = __builtin_amdgcn_readfirstlane(t >> 6);  // uniform per wave
   const int wm = wid / WAVES_N, wn = wid % WAVES_N;
   const FragOffsets fo = frag_offsets(lane, wm, wn);
   const uint32_t lds0 = lds_addr(lds);
   const int64_t nrows = kMasked ? capacity : min((int64_t)status[0], capacity);
-  const int sbytes = kFmt == kU8 ? 1 : (kFmt == kF32 ? 4 : 0);
+  const int sbytes = kFmt == kU8 ? 1 : (kFmt == kF32 || kFmt == kMX ? 4 : 0);
   const int KB = K / BK, NT = N / BN;
 
   // Row groups: expert e's block [start_e, end_e) (clamped to the valid rows)
@@ -685,6 +779,8 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(
     it.na_slots = act_slots(it.na);
     it.a = a + m0 * K;
     it.b = w + ((int64_t)e * N + (int64_t)nt * BN) * K;
+    it.ws = kFmt == kMX ? w_scale + ((int64_t)e * N + (int64_t)nt * BN) * (K / 32) : nullptr;
+    it.wsc_lds = lds_addr(wsc);
     it.as = a_scale + m0 * sbytes;
     it.as_kstride = capacity * sbytes;
     {
@@ -761,8 +857,9 @@ moe_status launch_gemm(bool masked, const void* a, const void* a_scale, int kind
   int64_t grid = device_cus();
   if (grid > max_items) grid = max_items;
   grid = (grid + kXcds - 1) / kXcds * kXcds;
-  auto kern = kind == kU8   ? (masked ? grouped_gemm_kernel<kU8, true>
-                                       : grouped_gemm_kernel<kU8, false>)
+  auto kern = kind == kMX   ? grouped_gemm_kernel<kMX, false>
+              : kind == kU8 ? (masked ? grouped_gemm_kernel<kU8, true>
+                                      : grouped_gemm_kernel<kU8, false>)
               : kind == kBF ? (masked ? grouped_gemm_kernel<kBF, true>
                                       : grouped_gemm_kernel<kBF, false>)
                             : (masked ? grouped_gemm_kernel<kF32, true>
@@ -788,16 +885,19 @@ extern "C" moe_status moe_grouped_gemm_fp8(const void* a, const void* a_scale, m
   if (align < MOE_MIN_ALIGN || align > MOE_MAX_ALIGN || (align & (align - 1)))
     return MOE_ERR_UNSUPPORTED;
   if (capacity % align != 0) return MOE_ERR_SHAPE;
-  if (fmt != MOE_SCALE_F32 && fmt != MOE_SCALE_UE8M0) return MOE_ERR_UNSUPPORTED;
+  if (fmt != MOE_SCALE_F32 && fmt != MOE_SCALE_UE8M0 && fmt != MOE_SCALE_MXFP8)
+    return MOE_ERR_UNSUPPORTED;
+  if (fmt == MOE_SCALE_MXFP8 && num_experts > kMxMaxExperts) return MOE_ERR_UNSUPPORTED;
   if (!psum || !status || !w || !w_scale) return MOE_ERR_NULL;
   if (capacity > 0 && (!a || !a_scale || !out)) return MOE_ERR_NULL;
   if (k / BK > MAX_KB) return MOE_ERR_UNSUPPORTED;
   if (((uintptr_t)a % 16) || ((uintptr_t)w % 16) || ((uintptr_t)out % 16) ||
-      ((uintptr_t)a_scale % (fmt == MOE_SCALE_F32 ? 16 : 4)) || ((uintptr_t)w_scale % 4))
+      ((uintptr_t)a_scale % (fmt == MOE_SCALE_UE8M0 ? 4 : 16)) || ((uintptr_t)w_scale % 4))
     return MOE_ERR_ALIGNMENT;
   if (capacity == 0) return MOE_OK;
-  return launch_gemm(false, a, a_scale, fmt == MOE_SCALE_UE8M0 ? kU8 : kF32, w, w_scale, psum,
-                     status, capacity, n, k, num_experts, align, out, stream);
+  const int kind = fmt == MOE_SCALE_MXFP8 ? kMX : (fmt == MOE_SCALE_UE8M0 ? kU8 : kF32);
+  return launch_gemm(false, a, a_scale, kind, w, w_scale, psum, status, capacity, n, k,
+                     num_experts, align, out, stream);
 }
 
 extern "C" moe_status moe_grouped_gemm_bf16(const void* a, const void* w, const int32_t* psum,

@@ -660,12 +660,18 @@ moe_status expand_layout(bool bf16, const void* x, int64_t x_stride, const void*
   if (align < MOE_MIN_ALIGN || align > MOE_MAX_ALIGN || (align & (align - 1)))
     return MOE_ERR_UNSUPPORTED;
   if (capacity % align != 0) return MOE_ERR_SHAPE;
-  if (fmt != MOE_SCALE_F32 && fmt != MOE_SCALE_UE8M0 && !(bf16 && fmt == MOE_SCALE_NONE))
+  if (fmt != MOE_SCALE_F32 && fmt != MOE_SCALE_UE8M0 && !(bf16 && fmt == MOE_SCALE_NONE) &&
+      !(!bf16 && fmt == MOE_SCALE_MXFP8))
     return MOE_ERR_UNSUPPORTED;
+  // MXFP8: a row's four 1x32 scale bytes of a 128-wide block travel as one
+  // 4-byte word (the fp32 path's copy); x_scale_stride is then in bytes.
+  const bool mx = fmt == MOE_SCALE_MXFP8;
   const bool keep = fmt == MOE_SCALE_NONE;  // bf16 rows copied as they are
   if (x_stride < (bf16 ? 2 * (int64_t)hidden : hidden) ||
-      (!bf16 && x_scale_stride < hidden / kGroup))
+      (!bf16 && x_scale_stride < (mx ? hidden / 32 : hidden / kGroup)) ||
+      (mx && x_scale_stride % 4))
     return MOE_ERR_SHAPE;
+  if (mx && ((uintptr_t)x_scale % 4)) return MOE_ERR_ALIGNMENT;
   if (num_src_ranks < 0 || (psum_recv_per_rank && num_src_ranks == 0)) return MOE_ERR_SHAPE;
   if (!psum || !m_indices || !src2dst || !status) return MOE_ERR_NULL;
   if (rows > 0 && (!x || (!bf16 && !x_scale) || !topk_ids)) return MOE_ERR_NULL;
@@ -680,7 +686,7 @@ moe_status expand_layout(bool bf16, const void* x, int64_t x_stride, const void*
   const int E = num_experts;
   const int64_t ng = num_groups(rows);
   Workspace w = carve(workspace, rows, E);
-  const int scale_bytes = keep ? 0 : (fmt == MOE_SCALE_F32 ? 4 : 1);
+  const int scale_bytes = keep ? 0 : (fmt == MOE_SCALE_F32 || mx ? 4 : 1);
 
   const int G = groups_per_block(E);
   const int64_t nb = num_blocks(rows, E);
@@ -713,7 +719,8 @@ moe_status expand_layout(bool bf16, const void* x, int64_t x_stride, const void*
   hipLaunchKernelGGL(scatter,
                      dim3((unsigned)grid), dim3(kScatterThreads), lds, s,
                      (const uint8_t*)x, x_stride, (const uint8_t*)x_scale,
-                     x_scale_stride * scale_bytes, scale_bytes, topk_ids, topk_weights,
+                     mx ? x_scale_stride : x_scale_stride * scale_bytes, scale_bytes, topk_ids,
+                     topk_weights,
                      psum_recv_per_rank, num_src_ranks, rows, keep ? 2 * hidden : hidden, topk, E,
                      capacity, align, w.grp, w.blk, G, (int)nb, w.blk_flag, fold ? 1 : 0,
                      w.starts, w.padbase,

@@ -110,9 +110,20 @@ typedef enum {
 typedef enum {
   MOE_SCALE_F32 = 0,        /* fp32 scale per group                       */
   MOE_SCALE_UE8M0 = 1,      /* one power-of-two exponent byte per group   */
-  MOE_SCALE_NONE = 2        /* moe_expand_layout_bf16 only: keep the rows in
+  MOE_SCALE_NONE = 2,       /* moe_expand_layout_bf16 only: keep the rows in
                                bf16, no quantisation, no scales (the bf16-
                                weight path)                               */
+  MOE_SCALE_MXFP8 = 3       /* MXFP8: one UE8M0 byte per 1x32 group along K,
+                               for activations and for every weight row
+                               [P3 DeepGemmMoeQuantInfo: block [1, 32]];
+                               activation scales [rows, K/32] bytes
+                               (x_scale_stride in bytes, a multiple of 4),
+                               expanded ones as one 4-byte word per
+                               (128-wide K block, row): the block's four
+                               bytes in K order, K-block-major; weight
+                               scales [E, N, K/32] bytes.  Supported by
+                               moe_expand_layout, moe_grouped_gemm_fp8 (at
+                               most 256 experts), moe_act_quant (no fold)  */
 } moe_scale_fmt;
 
 /* Bits of status[1] written by moe_expand_layout. */

@@ -81,6 +81,8 @@ def test_layout_rejects_bad_arguments():
     assert _layout(align=8) == M.MOE_ERR_UNSUPPORTED
     assert _layout(cap=100) == M.MOE_ERR_SHAPE
     assert _layout(fmt=7) == M.MOE_ERR_UNSUPPORTED
+    assert _layout(fmt=3, x_scale_stride=6) == M.MOE_ERR_SHAPE    # MXFP8: >= H/32 bytes
+    assert _layout(fmt=3, x_scale_stride=10) == M.MOE_ERR_SHAPE   # ... and a multiple of 4
     assert _layout(x_stride=128) == M.MOE_ERR_SHAPE
     assert _layout(prank=FAKE, nsrc=0) == M.MOE_ERR_SHAPE
     assert _layout(psum=None) == M.MOE_ERR_NULL
@@ -105,7 +107,8 @@ def test_gemm_rejects_bad_arguments():
     assert call(k=192) == M.MOE_ERR_SHAPE
     assert call(cap=100) == M.MOE_ERR_SHAPE
     assert call(align=24) == M.MOE_ERR_UNSUPPORTED
-    assert call(fmt=3) == M.MOE_ERR_UNSUPPORTED
+    assert call(fmt=9) == M.MOE_ERR_UNSUPPORTED
+    assert call(fmt=3, E=300) == M.MOE_ERR_UNSUPPORTED   # MXFP8: at most 256 experts
     assert call(psum=None) == M.MOE_ERR_NULL
     assert call(as_=FAKE + 2) == M.MOE_ERR_ALIGNMENT
     assert call(as_=FAKE + 4) == M.MOE_ERR_ALIGNMENT        # fp32 scales: 16 bytes

@@ -34,6 +34,8 @@ std_bf16_tiny      standard path with bf16 weights (no quantisation
                    anywhere): std_tiny's shape
 std_dsv3_bf16      standard single-GPU MoE, DeepSeek-V3 shape, bf16
                    weights (256 experts, 22.5 GB), factor 2.5
+dsv3_mxfp8         as dsv3 with MXFP8 operands (1x32 UE8M0 groups for the
+                   activations and every weight row)
 dsv3_decode        decode share on the masked slab: 1024 received rows
                    (32 tokens from each of 32 source ranks), H=7168,
                    I=2048, 8 local of 256 experts, top-8 uniform,
@@ -100,6 +102,8 @@ WORKLOADS = {
                               input="bf16", routed_scale=2.5, weights="bf16"),
     "std_dsv3_bf16": Workload("std_dsv3_bf16", 4096, 7168, 2048, 256, 256, 8, 128,
                               seed=1010, input="bf16", routed_scale=2.5, weights="bf16"),
+    "dsv3_mxfp8": Workload("dsv3_mxfp8", 4096, 7168, 2048, 8, 256, 8, 128, fmt="mxfp8",
+                           seed=1011),
     "dsv3_decode": Workload("dsv3_decode", 1024, 7168, 2048, 8, 256, 8, 128,
                             seed=1008, max_m=128),
 }
