@@ -19,6 +19,12 @@
 //    an (expert, N tile) stream the same weights side by side and that XCD's
 //    L2 serves them, while neighbouring N tiles share the groups'
 //    activations.
+//  - Each N tile walks K from its own start block, k0 = nt * KB / NT, wrapping
+//    round: the items of one row group (one XCD at the DeepSeek-V3 share)
+//    would otherwise all ask for the same activation block at once and all
+//    wait out its HBM miss; staggered, one of them misses and the rest find
+//    it in L2.  The start depends only on the N tile, so the contiguous and
+//    masked modes still sum each output in the same order.
 //  - K advances one 128-wide scale block per step = one
 //    v_mfma_scale_f32_16x16x128_f8f6f4 per 16x16 sub-tile.  Eight waves (two
 //    per SIMD) in a 4 x 2 grid, each owning 64 x 64 outputs (4 x 4 MFMA tiles).
@@ -208,6 +214,7 @@ struct Item {
   int live;             // rows of the group that hold a slot (1..GM); the
                         // rest of the group is alignment padding
   int KB;               // K / 128
+  int k0;               // first K block of this item's walk (then k0+1, .., wrapping)
   int K;
   int sbytes;           // 4 (fp32, MXFP8 words) or 1 (UE8M0)
   const uint8_t* ws;    // MXFP8: scales of the N tile's first weight row (K/32 bytes per row)
@@ -390,9 +397,10 @@ struct StepScales<kF32, NFM> {
   float raw[NFM];  // activation scale of this lane's row, per row tile
   float wraw;      // the weight block scale
   float scl[NFM];  // their products
-  __device__ __forceinline__ void read(uint32_t sc, uint32_t bsc, const Item&,
+  __device__ __forceinline__ void read(uint32_t sc, uint32_t bsc, const Item& it,
                                        const FragOffsets& fo, int kb, int) {
-    wraw = lds_load<float>(bsc + kb * 4);
+    const int blk = kb + it.k0 < it.KB ? kb + it.k0 : kb + it.k0 - it.KB;
+    wraw = lds_load<float>(bsc + blk * 4);
 #pragma unroll
     for (int i = 0; i < NFM; ++i) raw[i] = lds_load<float>(sc + (fo.m_row + i * ROW_TILE_STRIDE) * 4);
   }
@@ -432,7 +440,8 @@ struct StepScales<kU8, NFM> {
   __device__ __forceinline__ void read(uint32_t sc, uint32_t bsc, const Item& it,
                                        const FragOffsets& fo, int kb, int lane) {
     const int arow = fo.m_row;  // this lane's activation row
-    wraw = lds_load<uint32_t>(bsc + ((it.bs_skew + kb) & ~3));
+    const int blk = kb + it.k0 < it.KB ? kb + it.k0 : kb + it.k0 - it.KB;
+    wraw = lds_load<uint32_t>(bsc + ((it.bs_skew + blk) & ~3));
 #pragma unroll
     for (int i = 0; i < NFM; ++i)
       raw[i] = lds_load<uint32_t>(sc + ((arow + i * ROW_TILE_STRIDE) & ~3));
@@ -440,7 +449,7 @@ struct StepScales<kU8, NFM> {
   __device__ __forceinline__ void finish(const Item& it, const FragOffsets& fo, int kb,
                                          int lane) {
     const int arow = fo.m_row;
-    const int bpos = it.bs_skew + kb;
+    const int bpos = it.bs_skew + (kb + it.k0 < it.KB ? kb + it.k0 : kb + it.k0 - it.KB);
     sbyte = (int)((wraw >> (8 * (bpos & 3))) & 0xffu);
 #pragma unroll
     for (int i = 0; i < NFM; ++i)
@@ -581,13 +590,14 @@ __device__ __forceinline__ void kloop(uint32_t lds0, v4f (&acc)[FM][FN], const I
   const uint32_t a_end = lds0 + A_BASE + (uint32_t)(it.na_slots * it.a_slot_bytes);
   // Stream state: source pointers and destination slots of the next stage to
   // load, advanced one stage per issue.
-  const uint8_t* src = uniform_ptr(kW ? it.b : it.a);
-  const uint8_t* ssrc = uniform_ptr(it.as);
+  int blk = it.k0;  // K block of the next stage to load
+  const uint8_t* src = uniform_ptr((kW ? it.b : it.a) + (int64_t)it.k0 * BK);
+  const uint8_t* ssrc = uniform_ptr(it.as + it.k0 * it.as_kstride);
   uint32_t dst = kW ? lds0 : lds0 + A_BASE, sdst = lds0 + SC_BASE;
   // MXFP8 weight waves: wave wid brings weight rows wid * 32 .. + 31's scale
   // words of each stage (lanes 32-63 repeat lanes 0-31 into the upper half of
   // its 256 bytes) into the slot that matches the weight slot.
-  const uint8_t* wsrc = kMxW ? uniform_ptr(it.ws) : nullptr;
+  const uint8_t* wsrc = kMxW ? uniform_ptr(it.ws + it.k0 * 4) : nullptr;
   const uint32_t wbase = kMxW ? it.wsc_lds + (uint32_t)wid * 256u : 0u;
   uint32_t wdst = wbase;
   auto issue = [&]() __attribute__((always_inline)) {
@@ -596,7 +606,7 @@ __device__ __forceinline__ void kloop(uint32_t lds0, v4f (&acc)[FM][FN], const I
       dst = dst + B_BYTES == lds0 + B_RING ? lds0 : dst + B_BYTES;
       if constexpr (kMxW) {
         dma4(wsrc, wl.wsc_off, wdst);
-        wsrc += 4;
+        wsrc += blk + 1 == KB ? 4 - 4 * KB : 4;
         wdst = wdst + WSC_SLOT == wbase + kBSlots * WSC_SLOT ? wbase : wdst + WSC_SLOT;
       }
     } else {
@@ -604,9 +614,10 @@ __device__ __forceinline__ void kloop(uint32_t lds0, v4f (&acc)[FM][FN], const I
       dst = dst + it.a_slot_bytes == a_end ? lds0 + A_BASE : dst + it.a_slot_bytes;
       sdst = sdst + SC_SLOT == lds0 + SC_BASE + kScSlots * SC_SLOT ? lds0 + SC_BASE
                                                                     : sdst + SC_SLOT;
-      ssrc += it.as_kstride;
+      ssrc += blk + 1 == KB ? it.as_kstride * (1 - KB) : it.as_kstride;
     }
-    src += BK;
+    src += blk + 1 == KB ? (int64_t)BK * (1 - KB) : (int64_t)BK;
+    blk = blk + 1 == KB ? 0 : blk + 1;
   };
   // Read-side slots of stage kb+1.
   uint32_t rb = lds0 + B_BYTES, ra = lds0 + A_BASE + it.a_slot_bytes;
@@ -772,6 +783,7 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(
     it.live = (int)live;
     it.K = K;
     it.KB = KB;
+    it.k0 = (int)(((int64_t)nt * KB) / NT);  // staggered K start (see the header)
     it.sbytes = sbytes;
     it.blocks = ((int)live + 7) >> 3;
     it.na = (it.blocks + kLoadWaves - 1) / kLoadWaves;  // 1..8
