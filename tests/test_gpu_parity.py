@@ -126,6 +126,10 @@ SMALL = [
     # large for the scatter to scan itself, so the separate scan kernel runs
     ("tiny", dict(rows=3600, hidden=128, inter=128, experts=300, global_experts=600, topk=4,
                   align=16, seed=83)),
+    # the most local experts the library takes (MOE_MAX_EXPERTS = 1024), every
+    # expert local, ~16 rows each: the GEMM's expert tables at their full size
+    ("tiny", dict(rows=2048, hidden=128, inter=128, experts=1024, global_experts=1024, topk=8,
+                  align=16, seed=84)),
 ]
 IDS = [f"{n}-{'-'.join(f'{k}{v}' for k, v in o.items())}" for n, o in SMALL]
 

@@ -118,6 +118,7 @@ def _check_invariants(ids, w, x, xs, nv, E, align):
 @pytest.mark.parametrize("seed,rows,topk,E,align,nv", [
     (0, 37, 3, 5, 4, 37), (1, 64, 2, 4, 64, 64), (2, 100, 8, 8, 16, 71),
     (3, 9, 4, 3, 2, 0), (4, 50, 1, 1, 8, 50), (5, 200, 6, 16, 32, 150),
+    (6, 300, 8, 1024, 16, 300),   # the most local experts, most of them empty
 ])
 def test_layout_invariants(seed, rows, topk, E, align, nv):
     ids, w = _random_case(seed, rows, topk, E, align)
