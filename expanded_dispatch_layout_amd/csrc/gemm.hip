@@ -315,7 +315,7 @@ struct WaveLoads {
 struct FragOffsets {
   int a_lo, a_hi, b_lo, b_hi, m_row;
   int wsc_lane;  // MXFP8: this lane's weight row's word in a weight-scale slot (column tile 0)
-  int a_mx[4], b_mx[4];  // MXFP8: the four 8-byte pieces of this lane's fragments
+  int a_mx_lo, a_mx_hi, b_mx_lo, b_mx_hi;  // MXFP8: this lane's two 16-byte chunks
 };
 
 __device__ __forceinline__ FragOffsets frag_offsets(int lane, int wm, int wn) {
@@ -337,26 +337,14 @@ __device__ __forceinline__ FragOffsets frag_offsets(int lane, int wm, int wn) {
   // lane group g = lane / 16, with lane l's scale register scaling block g of
   // its row (measured on gfx950 with per-block scales on either operand,
   // against the two other plausible orders).  So lane l brings logical
-  // 16-byte chunks g and 4 + g.
-#pragma unroll
-  for (int q = 0; q < 4; ++q) {
-    const int c = (lane >> 4) + 4 * (q >> 1), h = (q & 1) * 8;
-    f.a_mx[q] = swz(ra, c) + h;
-    f.b_mx[q] = swz(rb, c) + h;
-  }
+  // 16-byte chunks g and 4 + g: two 16-byte reads per fragment, like the
+  // other formats, one logical chunk per 16 rows (bank-conflict free).
+  const int g = lane >> 4;
+  f.a_mx_lo = swz(ra, g);
+  f.a_mx_hi = swz(ra, 4 + g);
+  f.b_mx_lo = swz(rb, g);
+  f.b_mx_hi = swz(rb, 4 + g);
   return f;
-}
-
-typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
-__device__ __forceinline__ v8i frag4x8(uint32_t base, const int (&off)[4]) {
-  v8i r;
-#pragma unroll
-  for (int q = 0; q < 4; ++q) {
-    const u32x2 p = lds_load<u32x2>(base + off[q]);
-    r[2 * q] = (int)p[0];
-    r[2 * q + 1] = (int)p[1];
-  }
-  return r;
 }
 
 __device__ __forceinline__ v8i frag2(uint32_t base, int lo_off, int hi_off) {
@@ -476,8 +464,8 @@ __device__ __forceinline__ void step(v8i (&a)[FM], v8i (&b)[FN], v4f (&acc)[FM][
     if constexpr (kNext) {
       const int i = t / FN, j = t % FN;
       if constexpr (kFmt == kMX) {
-        if (i == NFM - 1) b[j] = frag4x8(next_b + j * 2048, fo.b_mx);
-        if (j == FN - 1) a[i] = frag4x8(next_a + i * A_TILE_STRIDE, fo.a_mx);
+        if (i == NFM - 1) b[j] = frag2(next_b + j * 2048, fo.b_mx_lo, fo.b_mx_hi);
+        if (j == FN - 1) a[i] = frag2(next_a + i * A_TILE_STRIDE, fo.a_mx_lo, fo.a_mx_hi);
       } else {
         if (i == NFM - 1) b[j] = frag2(next_b + j * 2048, fo.b_lo, fo.b_hi);
         if (j == FN - 1) a[i] = frag2(next_a + i * A_TILE_STRIDE, fo.a_lo, fo.a_hi);
@@ -639,12 +627,13 @@ __device__ __forceinline__ void kloop(uint32_t lds0, v4f (&acc)[FM][FN], const I
   if constexpr (NFM > 0) {
 #pragma unroll
     for (int j = 0; j < FN; ++j) {
-      if constexpr (kFmt == kMX) b[j] = frag4x8(lds0 + j * 2048, fo.b_mx);
+      if constexpr (kFmt == kMX) b[j] = frag2(lds0 + j * 2048, fo.b_mx_lo, fo.b_mx_hi);
       else b[j] = frag2(lds0 + j * 2048, fo.b_lo, fo.b_hi);
     }
 #pragma unroll
     for (int i = 0; i < NFM; ++i) {
-      if constexpr (kFmt == kMX) a[i] = frag4x8(lds0 + A_BASE + i * A_TILE_STRIDE, fo.a_mx);
+      if constexpr (kFmt == kMX) a[i] = frag2(lds0 + A_BASE + i * A_TILE_STRIDE, fo.a_mx_lo,
+                                              fo.a_mx_hi);
       else a[i] = frag2(lds0 + A_BASE + i * A_TILE_STRIDE, fo.a_lo, fo.a_hi);
     }
     if constexpr (kFmt == kMX) {
