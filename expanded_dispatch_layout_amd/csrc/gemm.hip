@@ -399,21 +399,28 @@ struct StepScales<kF32, NFM> {
 };
 template <int NFM>
 struct StepScales<kMX, NFM> {  // MXFP8: per-lane bytes of its rows' 32-wide K chunk
-  int abyte[NFM];  // this lane's activation row, per row tile
+  int abyte[NFM];  // this lane's activation row, per row tile (the step computed)
   int sbyte[FN];   // this lane's weight row, per column tile
-  // Step kb's bytes, read straight into the registers its MFMAs take: lane l
-  // holds K chunk l / 16 of the step, which is byte l / 16 of its rows'
-  // words.  Issued after the step before has issued its last MFMA; the LDS
-  // wait before the next barrier covers them (only one step's bytes live).
+  int nabyte[NFM], nsbyte[FN];  // the same for the next step
+  // Step kb's bytes: lane l holds K chunk l / 16 of the step, which is byte
+  // l / 16 of its rows' words.  Read into the next-step registers early in
+  // the step before (its stage has landed by then), moved into the ones the
+  // MFMAs take after that step's last MFMA.
   __device__ __forceinline__ void load(uint32_t sc, const Item& it, const FragOffsets& fo,
                                        int kb, int lane) {
     const uint32_t ws = it.wsc_lds + (uint32_t)(kb % kBSlots) * WSC_SLOT + (lane >> 4);
 #pragma unroll
     for (int j = 0; j < FN; ++j)
-      sbyte[j] = lds_load<uint8_t>(ws + fo.wsc_lane + (j >> 1) * 256 + (j & 1) * 64);
+      nsbyte[j] = lds_load<uint8_t>(ws + fo.wsc_lane + (j >> 1) * 256 + (j & 1) * 64);
 #pragma unroll
     for (int i = 0; i < NFM; ++i)
-      abyte[i] = lds_load<uint8_t>(sc + (fo.m_row + i * ROW_TILE_STRIDE) * 4 + (lane >> 4));
+      nabyte[i] = lds_load<uint8_t>(sc + (fo.m_row + i * ROW_TILE_STRIDE) * 4 + (lane >> 4));
+  }
+  __device__ __forceinline__ void advance() {
+#pragma unroll
+    for (int j = 0; j < FN; ++j) sbyte[j] = nsbyte[j];
+#pragma unroll
+    for (int i = 0; i < NFM; ++i) abyte[i] = nabyte[i];
   }
   __device__ __forceinline__ void read(uint32_t, uint32_t, const Item&, const FragOffsets&, int,
                                        int) {}
@@ -479,8 +486,10 @@ __device__ __forceinline__ void step(v8i (&a)[FM], v8i (&b)[FN], v4f (&acc)[FM][
     }
     if constexpr (kFmt == kU8 && kNext)
       if (t == M - 1) ss.finish(it, fo, kb + 1, lane);       // the next step's operands
-    if constexpr (kFmt == kMX && kNext)
-      if (t == M - 1) ss.load(next_sc, it, fo, kb + 1, lane);  // after the last MFMA
+    if constexpr (kFmt == kMX && kNext) {
+      if (t == 0) ss.load(next_sc, it, fo, kb + 1, lane);  // the next step's bytes
+      if (t == M - 1) ss.advance();                         // after the last MFMA
+    }
     if (t == (M > 1 ? 1 : 0)) issue();
   };
   if constexpr (kFmt == kBF) {
@@ -638,6 +647,7 @@ __device__ __forceinline__ void kloop(uint32_t lds0, v4f (&acc)[FM][FN], const I
     }
     if constexpr (kFmt == kMX) {
       ss.load(lds0 + SC_BASE, it, fo, 0, lane);
+      ss.advance();
     } else {
       ss.read(lds0 + SC_BASE, bsc, it, fo, 0, lane);
       if constexpr (kFmt == kU8) ss.finish(it, fo, 0, lane);
