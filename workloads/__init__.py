@@ -216,12 +216,17 @@ def generate(wl, with_weights: bool = True, with_x: bool = True):
 
 def poison_tail(data, x_q, x_s):
     """Overwrite rows past the boundary of quantised activations with the
-    drawn poison bytes (in place).  x_s may hold fp32 scales or UE8M0 bytes."""
+    drawn poison bytes (in place).  x_s may hold fp32 scales, UE8M0 bytes
+    (one per 1x128 group) or MXFP8 bytes (one per 1x32 group: the four bytes
+    of each drawn 32-bit word)."""
     nv = data["num_valid"]
     if "tail_x_bytes" not in data:
         return
     x_q[nv:] = data["tail_x_bytes"]
+    bits = data["tail_scale_bits"]
     if x_s.dtype == np.float32:
-        x_s[nv:] = data["tail_scale_bits"].view(np.float32)
+        x_s[nv:] = bits.view(np.float32)
+    elif x_s.shape[1] == 4 * bits.shape[1]:
+        x_s[nv:] = np.ascontiguousarray(bits).view(np.uint8).reshape(len(bits), -1)
     else:
-        x_s[nv:] = (data["tail_scale_bits"] & 0xFF).astype(np.uint8)
+        x_s[nv:] = (bits & 0xFF).astype(np.uint8)
