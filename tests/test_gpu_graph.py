@@ -65,7 +65,7 @@ def _replay_check(mod, call, bufs, inputs_a, inputs_b, out):
     assert not torch.equal(eager["a"].view(torch.int16), eager["b"].view(torch.int16))
 
 
-@pytest.mark.parametrize("fmt", ["f32", "ue8m0"])
+@pytest.mark.parametrize("fmt", ["f32", "ue8m0", "mxfp8"])
 def test_expand_path_graph_replay(fmt):
     a = make("tiny", rows=40, valid_rows=23, src_ranks=4, fmt=fmt, seed=61)
     b = make("tiny", rows=40, valid_rows=31, src_ranks=4, fmt=fmt, seed=62)
@@ -102,3 +102,44 @@ def test_masked_decode_path_graph_replay():
     def call():
         mod(bufs["x"], bufs["x_scale"], bufs["ids"], bufs["w"], None, out=out)
     _replay_check(mod, call, bufs, ins_a, ins_b, out)
+
+
+@pytest.mark.parametrize("fmt", ["f32", "ue8m0"])
+def test_standard_path_graph_replay(fmt):
+    """The standard path (bf16 rows quantised in the layout, routed factor)."""
+    from tests.test_gpu_standard import to_gpu_std
+    from tests.test_oracle_standard import std_inputs
+    a = std_inputs(fmt=fmt, rows=48, seed=65)
+    b = std_inputs(fmt=fmt, rows=48, seed=66)
+    ga, gb = to_gpu_std(a), to_gpu_std(b)
+    R, T = a["ids"].shape
+    mod = M.StandardMoE(R, T, ga["w13"], ga["w13_scale"], ga["w2"], ga["w2_scale"], a["align"],
+                        fmt, a["routed_scaling_factor"])
+    out = torch.zeros((R, mod.H), dtype=torch.bfloat16, device="cuda")
+    keys = ("x", "ids", "w")
+    bufs = {k: ga[k].clone() for k in keys}
+
+    def call():
+        mod(bufs["x"], bufs["ids"], bufs["w"], out=out)
+    _replay_check(mod, call, bufs, {k: ga[k] for k in keys}, {k: gb[k] for k in keys}, out)
+
+
+def test_bf16_weight_path_graph_replay():
+    from tests.test_gpu_bf16 import t16
+    from tests.test_oracle_bf16 import bf16_inputs
+    a = bf16_inputs(rows=48, seed=67)
+    b = bf16_inputs(rows=48, seed=68)
+    R, T = a["ids"].shape
+    mod = M.StandardBf16MoE(R, T, t16(a["w13_bf16"]), t16(a["w2_bf16"]), a["align"],
+                            a["routed_scaling_factor"])
+    out = torch.zeros((R, mod.H), dtype=torch.bfloat16, device="cuda")
+
+    def dev(inp):
+        return {"x": t16(inp["x_bf16"]), "ids": torch.from_numpy(inp["ids"]).cuda(),
+                "w": torch.from_numpy(inp["w"]).cuda()}
+    ga, gb = dev(a), dev(b)
+    bufs = {k: v.clone() for k, v in ga.items()}
+
+    def call():
+        mod(bufs["x"], bufs["ids"], bufs["w"], out=out)
+    _replay_check(mod, call, bufs, ga, gb, out)
