@@ -50,8 +50,9 @@
 //  - UE8M0 scales: the exponent bytes are the MFMA's hardware scale operands
 //    (the group's byte repeats over its four 32-wide sub-blocks), so the
 //    matrix core accumulates the scaled products directly.
-//  - The bf16 output tile is staged through LDS and written with 16-byte
-//    stores; rows past the group are never written.
+//  - The bf16 outputs go straight from the accumulators to memory, 8 bytes
+//    (4 columns of one row) per lane and tile; rows past the group are never
+//    written.
 //  - Masked mode (the decode path's fixed-height slab, SGLang
 //    moe_runner/deep_gemm.py source, _run_masked_gemm; SGLang PR 37261, "Why
 //    decode stays on V1 low_latency"): expert e owns slab rows
@@ -95,10 +96,7 @@ constexpr int B_BYTES = BN * BK;             // 16 KB: one K block of the N tile
 // slots sized to the group, loaded 1..3 steps ahead (with the activation
 // scales) by waves 4-7.  vmcnt is per wave, so each stream keeps its own
 // depth.
-#ifndef GEMM_B_SLOTS
-#define GEMM_B_SLOTS 5
-#endif
-constexpr int kBSlots = GEMM_B_SLOTS;
+constexpr int kBSlots = 5;
 constexpr int B_RING = kBSlots * B_BYTES;
 constexpr int A_BASE = B_RING;
 constexpr int A_RING = 2 * A_BYTES;          // two slots of a full group, more if smaller
@@ -117,7 +115,6 @@ constexpr int kLoadWaves = 4;                // waves per stream: 0-3 weights, 4
 constexpr int B_LOADS = B_BYTES / (kLoadWaves * 64 * 16);  // 16-byte loads per lane per stage
 constexpr int A_LOADS = A_BYTES / (kLoadWaves * 64 * 16);  // at most, for a full group
 constexpr int W_LOADS = B_LOADS;             // a weight wave's loads per stage
-static_assert(GM * BN * 2 <= DATA_BYTES, "output tile must fit in LDS");
 static_assert(kWaves == 2 * kLoadWaves && B_LOADS == 4 && A_LOADS == 8, "load split");
 
 // Physical 16-byte chunk of logical chunk c in row r of a [rows][128 B] tile:
