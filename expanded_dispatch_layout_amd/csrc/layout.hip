@@ -36,6 +36,13 @@
 // quantises it per 1x128 group in registers (16 lanes per group, max by
 // xor-shuffles) and writes the codes and the group scales to every
 // destination, so the quantised rows never make a round trip through HBM.
+// With MOE_SCALE_NONE (bf16 weights) the bf16 rows are copied as they are
+// (the fp8 byte-copy scatter over rows of 2 * H bytes, no scales).
+//
+// MXFP8 (SGLang moe_runner/deep_gemm.py source, DeepGemmMoeQuantInfo: block
+// shape [1, 32], UE8M0 scales): the received scales are one byte per 1x32
+// group; the scatter copies each 128-wide block's four bytes as one 4-byte
+// word, K-block-major like the other formats' scales.
 #include "common.hpp"
 
 namespace moe {
