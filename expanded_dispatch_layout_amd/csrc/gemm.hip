@@ -19,12 +19,16 @@
 //    an (expert, N tile) stream the same weights side by side and that XCD's
 //    L2 serves them, while neighbouring N tiles share the groups'
 //    activations.
-//  - Each N tile walks K from its own start block, k0 = nt * KB / NT, wrapping
-//    round: the items of one row group (one XCD at the DeepSeek-V3 share)
-//    would otherwise all ask for the same activation block at once and all
-//    wait out its HBM miss; staggered, one of them misses and the rest find
-//    it in L2.  The start depends only on the N tile, so the contiguous and
-//    masked modes still sum each output in the same order.
+//  - In the workgroups' first round of items each N tile walks K from its own
+//    start block, k0 = nt * KB / NT, wrapping round: every CU starts at the
+//    same moment, and the items of one row group (one XCD at the
+//    DeepSeek-V3 share) would otherwise all ask for the same activation
+//    block at once and all wait out its HBM miss; staggered, one of them
+//    misses and the rest find it in L2.  Later rounds are out of phase
+//    already and walk K in order (a staggered walk there only lengthens
+//    each activation block's reuse distance in L2).  An output's summation
+//    order thus depends only on its N tile and its item's round, the same in
+//    the contiguous and masked modes when the item falls in the same round.
 //  - K advances one 128-wide scale block per step = one
 //    v_mfma_scale_f32_16x16x128_f8f6f4 per 16x16 sub-tile.  Eight waves (two
 //    per SIMD) in a 4 x 2 grid, each owning 64 x 64 outputs (4 x 4 MFMA tiles).
@@ -779,7 +783,8 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(
     it.live = (int)live;
     it.K = K;
     it.KB = KB;
-    it.k0 = (int)(((int64_t)nt * KB) / NT);  // staggered K start (see the header)
+    // Staggered K start for the first round (see the header).
+    it.k0 = item < (int64_t)gridDim.x ? (int)(((int64_t)nt * KB) / NT) : 0;
     it.sbytes = sbytes;
     it.blocks = ((int)live + 7) >> 3;
     it.na = (it.blocks + kLoadWaves - 1) / kLoadWaves;  // 1..8
