@@ -7,7 +7,8 @@ binding raises if the library is missing: there is no fallback.
 
 Functions mirror the C ABI in ``include/moe_expand.h``:
 
-    moe_expand_layout, moe_expand_layout_bf16, moe_grouped_gemm_fp8,
+    moe_expand_layout, moe_expand_layout_noalloc, moe_expand_layout_bf16,
+    moe_grouped_gemm_fp8,
     moe_act_quant, moe_gather, moe_expand_to_masked_slab,
     moe_grouped_gemm_fp8_masked, moe_act_quant_masked, moe_masked_slab_to_expand,
     moe_grouped_gemm_bf16, moe_silu_mul_bf16,
@@ -30,7 +31,8 @@ LIB_PATH = os.path.join(_HERE, "libmoe_expand.so")
 HEADER_PATH = os.path.join(os.path.dirname(_HERE), "include", "moe_expand.h")
 
 MOE_OK, MOE_ERR_NULL, MOE_ERR_SHAPE, MOE_ERR_ALIGNMENT = 0, 1, 2, 3
-MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE, MOE_ERR_LAUNCH = 4, 5, 6
+MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE, MOE_ERR_LAUNCH, MOE_ERR_SCRATCH = 4, 5, 6, 7
+MOE_NOALLOC_SCRATCH_BYTES = 4 << 20
 MOE_SCALE_F32, MOE_SCALE_UE8M0, MOE_SCALE_NONE, MOE_SCALE_MXFP8 = 0, 1, 2, 3
 MOE_FLAG_CAPACITY_OVERFLOW, MOE_FLAG_EXPERT_ID_RANGE, MOE_FLAG_SLAB_OVERFLOW = 1, 2, 4
 FMT = {"f32": MOE_SCALE_F32, "ue8m0": MOE_SCALE_UE8M0, "none": MOE_SCALE_NONE,
@@ -47,6 +49,8 @@ _SIGNATURES = {
     "moe_expand_workspace_bytes": (_SZ, [_I64, _I, _I]),
     "moe_expand_layout": (_I, [_P, _I64, _P, _I64, _I, _P, _P, _P, _I, _I64, _I, _I,
                                _I, _I, _I64, _P, _P, _P, _P, _P, _P, _P, _P, _SZ, _P]),
+    "moe_expand_layout_noalloc": (_I, [_P, _I64, _P, _I64, _I, _P, _P, _P, _I, _I64, _I, _I,
+                                       _I, _I, _I64, _P, _P, _P, _P, _P, _P, _P, _P]),
     "moe_expand_layout_bf16": (_I, [_P, _I64, _I, _P, _P, _P, _I, _I64, _I, _I, _I, _I,
                                     _I64, _P, _P, _P, _P, _P, _P, _P, _P, _SZ, _P]),
     "moe_grouped_gemm_fp8": (_I, [_P, _P, _I, _P, _P, _P, _P, _I64, _I, _I, _I, _I,
@@ -143,6 +147,22 @@ def moe_expand_layout(x, x_scale, fmt, topk_ids, topk_weights, psum_recv_per_ran
         _ptr(row_weight), _ptr(status), _ptr(workspace),
         workspace.numel() * workspace.element_size(), _stream(stream))
     _check("moe_expand_layout", code)
+
+
+def moe_expand_layout_noalloc(x, x_scale, fmt, topk_ids, topk_weights, psum_recv_per_rank,
+                              num_experts, align, capacity, ex, ex_scale, psum, m_indices,
+                              src2dst, row_weight, status, stream=None):
+    """moe_expand_layout with the library's static per-GPU scratch as the
+    workspace: no workspace argument, nothing allocated (see moe_expand.h)."""
+    rows, hidden = topk_ids.shape[0], ex.shape[1]
+    code = lib().moe_expand_layout_noalloc(
+        _ptr(x), x.stride(0) * x.element_size(), _ptr(x_scale), x_scale.stride(0), _fmt(fmt),
+        _ptr(topk_ids), _ptr(topk_weights), _ptr(psum_recv_per_rank),
+        0 if psum_recv_per_rank is None else psum_recv_per_rank.numel(),
+        rows, hidden, topk_ids.shape[1], num_experts, align, capacity,
+        _ptr(ex), _ptr(ex_scale), _ptr(psum), _ptr(m_indices), _ptr(src2dst),
+        _ptr(row_weight), _ptr(status), _stream(stream))
+    _check("moe_expand_layout_noalloc", code)
 
 
 def moe_expand_layout_bf16(x, fmt, topk_ids, topk_weights, psum_recv_per_rank,

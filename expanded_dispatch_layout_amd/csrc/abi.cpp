@@ -13,6 +13,9 @@ extern "C" const char* moe_status_string(int status) {
     case MOE_ERR_UNSUPPORTED: return "unsupported argument combination";
     case MOE_ERR_WORKSPACE: return "workspace missing or too small";
     case MOE_ERR_LAUNCH: return "kernel launch failed";
+    case MOE_ERR_SCRATCH:
+      return "the sizes need more workspace than moe_expand_layout_noalloc's static scratch "
+             "holds (MOE_NOALLOC_SCRATCH_BYTES)";
     default: return "unknown status";
   }
 }

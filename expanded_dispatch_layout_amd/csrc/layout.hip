@@ -43,6 +43,8 @@
 // shape [1, 32], UE8M0 scales): the received scales are one byte per 1x32
 // group; the scatter copies each 128-wide block's four bytes as one 4-byte
 // word, K-block-major like the other formats' scales.
+#include <mutex>
+
 #include "common.hpp"
 
 namespace moe {
@@ -659,7 +661,7 @@ moe_status expand_layout(bool bf16, const void* x, int64_t x_stride, const void*
                          int align, int64_t capacity, void* ex, void* ex_scale, int32_t* psum,
                          int32_t* m_indices, int32_t* src2dst, float* row_weight,
                          int32_t* status, void* workspace, size_t workspace_bytes_,
-                         void* stream) {
+                         void* stream, void* (*scratch_fn)() = nullptr) {
   if (rows < 0 || hidden <= 0 || hidden % kGroup != 0 || topk < 1 || topk > MOE_MAX_TOPK ||
       num_experts < 1 || num_experts > MOE_MAX_EXPERTS || capacity < 0 || rows > (1LL << 30) ||
       capacity > (1LL << 30) || (int64_t)rows * topk > (1LL << 30))
@@ -685,6 +687,11 @@ moe_status expand_layout(bool bf16, const void* x, int64_t x_stride, const void*
   if (capacity > 0 && (!ex || (!keep && !ex_scale))) return MOE_ERR_NULL;
   if (row_weight && !topk_weights && rows > 0) return MOE_ERR_NULL;
   if ((x_stride % 16) || ((uintptr_t)x % 16) || ((uintptr_t)ex % 16)) return MOE_ERR_ALIGNMENT;
+  if (scratch_fn) {  // moe_expand_layout_noalloc: the static per-GPU scratch
+    if (workspace_bytes(rows, num_experts) > workspace_bytes_) return MOE_ERR_SCRATCH;
+    workspace = scratch_fn();
+    if (!workspace) return MOE_ERR_LAUNCH;
+  }
   if (!workspace || workspace_bytes_ < workspace_bytes(rows, num_experts))
     return MOE_ERR_WORKSPACE;
   if ((uintptr_t)workspace % 256) return MOE_ERR_ALIGNMENT;
@@ -763,4 +770,58 @@ extern "C" moe_status moe_expand_layout_bf16(
                        psum_recv_per_rank, num_src_ranks, rows, hidden, topk, num_experts, align,
                        capacity, ex, ex_scale, psum, m_indices, src2dst, row_weight, status,
                        workspace, workspace_bytes_, stream);
+}
+
+// ---- the layout with no workspace argument and no allocation ----
+//
+// For callers that cannot allocate (code under HIP graph capture, tight
+// serving loops, harnesses that forbid allocation): the workspace lives in a
+// file-scope device array of fixed size, one copy per GPU, held until the
+// process ends.  Host code never passes the array's name to a kernel (on the
+// host it is only a stand-in for the symbol): its device address is looked
+// up once per device with hipGetSymbolAddress, with that device current, and
+// that address is what the kernels get.  Every call on a GPU shares that
+// GPU's array, so calls that overlap on one GPU (different streams, no
+// ordering between them) race; calls ordered on one stream do not.  The
+// kernels overwrite every workspace entry they read before reading it, so
+// nothing needs clearing between calls.
+namespace {
+
+constexpr size_t kNoAllocScratchBytes = MOE_NOALLOC_SCRATCH_BYTES;
+static __device__ __align__(256) uint8_t scratch[kNoAllocScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// Device address of this device's copy of `scratch` (looked up on the first
+// call on each device); nullptr if the runtime cannot give it.
+void* scratch_address() {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_ptr[dev] == nullptr) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || p == nullptr)
+      return nullptr;
+    g_scratch_ptr[dev] = p;
+  }
+  return g_scratch_ptr[dev];
+}
+
+}  // namespace
+
+extern "C" moe_status moe_expand_layout_noalloc(
+    const void* x, int64_t x_stride, const void* x_scale, int64_t x_scale_stride,
+    moe_scale_fmt fmt, const int32_t* topk_ids, const float* topk_weights,
+    const int32_t* psum_recv_per_rank, int num_src_ranks, int64_t rows, int hidden, int topk,
+    int num_experts, int align, int64_t capacity, void* ex, void* ex_scale, int32_t* psum,
+    int32_t* m_indices, int32_t* src2dst, float* row_weight, int32_t* status, void* stream) {
+  // Every argument is checked as in moe_expand_layout, before the scratch
+  // address is looked up; a valid request that needs more workspace than the
+  // array holds gets MOE_ERR_SCRATCH.
+  return expand_layout(false, x, x_stride, x_scale, x_scale_stride, fmt, topk_ids, topk_weights,
+                       psum_recv_per_rank, num_src_ranks, rows, hidden, topk, num_experts, align,
+                       capacity, ex, ex_scale, psum, m_indices, src2dst, row_weight, status,
+                       nullptr, kNoAllocScratchBytes, stream, scratch_address);
 }

@@ -104,7 +104,12 @@ typedef enum {
   MOE_ERR_ALIGNMENT = 3,    /* a pointer or stride is not 16-byte aligned */
   MOE_ERR_UNSUPPORTED = 4,  /* valid in principle, not supported          */
   MOE_ERR_WORKSPACE = 5,    /* workspace missing or too small             */
-  MOE_ERR_LAUNCH = 6        /* a kernel launch failed                     */
+  MOE_ERR_LAUNCH = 6,       /* a kernel launch (or, for
+                               moe_expand_layout_noalloc, the lookup of its
+                               scratch address) failed                    */
+  MOE_ERR_SCRATCH = 7       /* moe_expand_layout_noalloc: the sizes need
+                               more workspace than its static scratch
+                               (MOE_NOALLOC_SCRATCH_BYTES) holds          */
 } moe_status;
 
 typedef enum {
@@ -141,6 +146,10 @@ typedef enum {
 #define MOE_MAX_TOPK 32
 #define MOE_MIN_ALIGN 16
 #define MOE_MAX_ALIGN 1024
+/* Size of moe_expand_layout_noalloc's static per-GPU scratch: calls with
+ * moe_expand_workspace_bytes(rows, topk, num_experts) above it are refused
+ * (roughly rows * num_experts <= 15 million). */
+#define MOE_NOALLOC_SCRATCH_BYTES (4u << 20)
 
 /* Text for a moe_status value (static storage; never NULL). */
 const char* moe_status_string(int status);
@@ -204,6 +213,33 @@ moe_status moe_expand_layout(
     void* ex, void* ex_scale, int32_t* psum, int32_t* m_indices,
     int32_t* src2dst, float* row_weight, int32_t* status,
     void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * moe_expand_layout with no workspace argument, for callers that cannot
+ * allocate device memory: code under HIP graph capture, tight serving loops,
+ * harnesses that forbid allocation.  Every other argument, output and error
+ * is as moe_expand_layout's; the call allocates and frees nothing.
+ *
+ * The workspace is a static device array of MOE_NOALLOC_SCRATCH_BYTES inside
+ * the library: each GPU the library runs on holds its own copy until the
+ * process ends.  Its address is looked up on the first call on each device
+ * (that call must have the device current, as every call must).  Sizes whose
+ * workspace (moe_expand_workspace_bytes) exceeds the array return
+ * MOE_ERR_SCRATCH before anything is launched; a failed address lookup
+ * returns MOE_ERR_LAUNCH.  All calls on one GPU share the array: calls that
+ * may run concurrently on one GPU (unordered streams) race and must not be
+ * issued; calls ordered on one stream are safe, and nothing needs clearing
+ * between them.
+ */
+moe_status moe_expand_layout_noalloc(
+    const void* x, int64_t x_stride, const void* x_scale,
+    int64_t x_scale_stride, moe_scale_fmt fmt,
+    const int32_t* topk_ids, const float* topk_weights,
+    const int32_t* psum_recv_per_rank, int num_src_ranks,
+    int64_t rows, int hidden, int topk, int num_experts, int align,
+    int64_t capacity,
+    void* ex, void* ex_scale, int32_t* psum, int32_t* m_indices,
+    int32_t* src2dst, float* row_weight, int32_t* status, void* stream);
 
 /*
  * Expanded layout of bf16 token rows, quantised on the way [P3

@@ -53,7 +53,7 @@ def test_workspace_bytes():
 
 
 def test_status_strings():
-    for c in range(7):
+    for c in range(8):
         assert M.status_string(c)
     assert M.status_string(99) == "unknown status"
 
@@ -92,6 +92,38 @@ def test_layout_rejects_bad_arguments():
     assert _layout(x_stride=264) == M.MOE_ERR_ALIGNMENT
     assert _layout(ws=None) == M.MOE_ERR_WORKSPACE
     assert _layout(wsb=16) == M.MOE_ERR_WORKSPACE     # everything else valid
+
+
+def _layout_noalloc(**kw):
+    a = dict(x=FAKE, x_stride=256, x_scale=FAKE, x_scale_stride=2, fmt=0, ids=FAKE,
+             w=FAKE, prank=None, nsrc=0, rows=64, hidden=256, topk=2, E=4, align=64,
+             cap=320, ex=FAKE, exs=FAKE, psum=FAKE, mi=FAKE, s2d=FAKE, rw=FAKE, st=FAKE,
+             stream=None)
+    a.update(kw)
+    return M.lib().moe_expand_layout_noalloc(
+        a["x"], a["x_stride"], a["x_scale"], a["x_scale_stride"], a["fmt"], a["ids"],
+        a["w"], a["prank"], a["nsrc"], a["rows"], a["hidden"], a["topk"], a["E"],
+        a["align"], a["cap"], a["ex"], a["exs"], a["psum"], a["mi"], a["s2d"], a["rw"],
+        a["st"], a["stream"])
+
+
+def test_layout_noalloc_rejects_bad_arguments():
+    """Same host checks as moe_expand_layout, all made before the scratch
+    address is looked up (no GPU is touched by any of these calls)."""
+    assert _layout_noalloc(hidden=100) == M.MOE_ERR_SHAPE
+    assert _layout_noalloc(E=2000) == M.MOE_ERR_SHAPE
+    assert _layout_noalloc(align=48) == M.MOE_ERR_UNSUPPORTED
+    assert _layout_noalloc(cap=100) == M.MOE_ERR_SHAPE
+    assert _layout_noalloc(psum=None) == M.MOE_ERR_NULL
+    assert _layout_noalloc(x=MIS) == M.MOE_ERR_ALIGNMENT
+    # valid, but the workspace would exceed the static scratch
+    rows, E = 1 << 20, 256
+    assert M.moe_expand_workspace_bytes(rows, 2, E) > M.MOE_NOALLOC_SCRATCH_BYTES
+    cap = M.moe_expand_capacity(rows, 2, E, 64)
+    assert _layout_noalloc(rows=rows, E=E, cap=cap) == M.MOE_ERR_SCRATCH
+    # the largest workload sizes fit
+    assert M.moe_expand_workspace_bytes(16384, 8, 16) <= M.MOE_NOALLOC_SCRATCH_BYTES
+    assert M.moe_expand_workspace_bytes(8192, 8, 1024) <= M.MOE_NOALLOC_SCRATCH_BYTES
 
 
 def test_gemm_rejects_bad_arguments():
