@@ -67,33 +67,56 @@ from . import fp8, quant
 from .layout import align_up
 
 
+def _per_expert(mi, live, fn, workers):
+    """Run fn(e, rows) for every expert e with rows (labelled e, and live when
+    given).  The experts are independent: with `workers` > 1 they run on a
+    thread pool (scheduling only; each expert's arithmetic is unchanged)."""
+    jobs = []
+    for e in np.unique(mi[mi >= 0]):
+        sel = mi == e
+        if live is not None:
+            sel &= live
+        rows = np.nonzero(sel)[0]
+        if len(rows):
+            jobs.append((int(e), rows))
+    if workers and workers > 1 and len(jobs) > 1:
+        from concurrent.futures import ThreadPoolExecutor
+        with ThreadPoolExecutor(max_workers=workers) as ex:
+            list(ex.map(lambda j: fn(*j), jobs))
+    else:
+        for j in jobs:
+            fn(*j)
+
+
 def grouped_gemm(a_q, a_s, w_q, w_s, m_indices, n_rows: int, fmt: str,
-                 live=None):
+                 live=None, workers=None):
     """out[m] = bf16(deq(a[m]) @ deq(w[m_indices[m]])^T) for m < n_rows with
     m_indices[m] >= 0 (and live[m], when given).  Other rows are NaN."""
     w_q = np.asarray(w_q)
     n_out = w_q.shape[1]
     out = np.full((n_rows, n_out), np.nan, dtype=np.float32)
     mi = np.asarray(m_indices)[:n_rows]
-    for e in np.unique(mi[mi >= 0]):
-        sel = mi == e
-        if live is not None:
-            sel &= live
-        rows = np.nonzero(sel)[0]
-        if len(rows) == 0:
-            continue
+
+    def one(e, rows):
         a = quant.dequant_rows(np.asarray(a_q)[rows], np.asarray(a_s)[rows], fmt)
         w = quant.dequant_block(w_q[e], np.asarray(w_s)[e], fmt)
         out[rows] = fp8.round_bf16(a @ w.T)
+    _per_expert(mi, live, one, workers)
     return out
 
 
 def silu_mul(g32, u32):
-    """silu(g) * u = g / (1 + exp(-g)) * u, each operation in float32."""
+    """silu(g) * u = g / (1 + exp(-g)) * u, each operation in float32.
+
+    exp(-g) is the correctly rounded float32 value (computed in float64 and
+    rounded once; float64's error is far below a float32 rounding step), so
+    that every one of the four operations is one float32 rounding of the
+    exact result.  (numpy's own float32 exp is up to two ulps off.)"""
     g = np.asarray(g32, dtype=np.float32)
     u = np.asarray(u32, dtype=np.float32)
     with np.errstate(over="ignore"):
-        den = (np.float32(1.0) + np.exp(-g)).astype(np.float32)
+        e = np.exp(-g.astype(np.float64)).astype(np.float32)
+        den = (np.float32(1.0) + e).astype(np.float32)
     return ((g / den).astype(np.float32) * u).astype(np.float32)
 
 
@@ -163,7 +186,7 @@ def gather(D, src2dst, num_valid: int, topk_weights=None, scale: float = 1.0):
     return fp8.round_bf16(acc)
 
 
-def layer(inp, mode: str = "auto", routed_scaling_factor: float = 1.0):
+def layer(inp, mode: str = "auto", routed_scaling_factor: float = 1.0, workers=None):
     """The whole path on one rank.  `inp` holds: x_q [R,H] u8, x_s, ids [R,T],
     w [R,T] f32, num_valid, w13_q [E,2I,H], w13_s, w2_q [E,H,I], w2_s,
     align, fmt ('f32' | 'ue8m0'), cap (optional).
@@ -172,6 +195,7 @@ def layer(inp, mode: str = "auto", routed_scaling_factor: float = 1.0):
     'post' (weight applied in the gather), or 'auto' (fold for fp32 scales,
     post for UE8M0, as the pages do).  routed_scaling_factor multiplies the
     gathered sum (the standard path's factor; 1 on the expand path).
+    workers: experts run on this many threads in the GEMMs (None: one).
     Returns a dict of every stage."""
     from .layout import expand, capacity
     fmt = inp["fmt"]
@@ -189,11 +213,11 @@ def layer(inp, mode: str = "auto", routed_scaling_factor: float = 1.0):
     n = min(lay["total"], cap)
     live = live_rows(lay["m_indices"], lay["psum"], align, n)
     G = grouped_gemm(lay["ex"], lay["ex_scale"], inp["w13_q"], inp["w13_s"],
-                     lay["m_indices"], n, fmt, live=live)
+                     lay["m_indices"], n, fmt, live=live, workers=workers)
     fold = lay["row_weight"] if mode == "fold" else None
     dq, ds = act_quant(G, live, fmt, fold_weight=fold)
     D = grouped_gemm(dq, ds, inp["w2_q"], inp["w2_s"], lay["m_indices"], n,
-                     fmt, live=live)
+                     fmt, live=live, workers=workers)
     out = gather(D, lay["src2dst"], nv,
                  topk_weights=None if mode == "fold" else inp["w"],
                  scale=routed_scaling_factor)
@@ -215,7 +239,7 @@ def quantize_input(x_bf16, num_valid: int, fmt: str):
     return x_q, x_s
 
 
-def bf16_grouped_gemm(a_bits, w_bits, m_indices, n_rows: int, live=None):
+def bf16_grouped_gemm(a_bits, w_bits, m_indices, n_rows: int, live=None, workers=None):
     """out[m] = bf16(a[m] @ w[m_indices[m]]^T) with bf16 operands (uint16
     bits), float64 products and sums, one rounding; rows that are not live or
     labelled -1 are NaN."""
@@ -223,16 +247,12 @@ def bf16_grouped_gemm(a_bits, w_bits, m_indices, n_rows: int, live=None):
     out = np.full((n_rows, w_bits.shape[1]), np.nan, dtype=np.float32)
     mi = np.asarray(m_indices)[:n_rows]
     a_bits = np.asarray(a_bits, dtype=np.uint16)
-    for e in np.unique(mi[mi >= 0]):
-        sel = mi == e
-        if live is not None:
-            sel &= live
-        rows = np.nonzero(sel)[0]
-        if len(rows) == 0:
-            continue
+
+    def one(e, rows):
         a = fp8.bf16_from_bits(a_bits[rows]).astype(np.float64)
         w = fp8.bf16_from_bits(w_bits[e]).astype(np.float64)
         out[rows] = fp8.round_bf16(a @ w.T)
+    _per_expert(mi, live, one, workers)
     return out
 
 
@@ -249,7 +269,7 @@ def silu_mul_bf16(G, live):
     return y
 
 
-def bf16_layer(inp):
+def bf16_layer(inp, workers=None):
     """The bf16-weight path: `inp` holds x_bf16 [R, H], ids, w, w13_bf16
     [E, 2I, H], w2_bf16 [E, H, I] (uint16 bits), align, optional
     routed_scaling_factor, num_valid and cap."""
@@ -265,9 +285,11 @@ def bf16_layer(inp):
     lay = expand(ids, inp["w"], x, no_scales, nv, E, align, cap)
     n = min(lay["total"], cap)
     live = live_rows(lay["m_indices"], lay["psum"], align, n)
-    G = bf16_grouped_gemm(lay["ex"], inp["w13_bf16"], lay["m_indices"], n, live=live)
+    G = bf16_grouped_gemm(lay["ex"], inp["w13_bf16"], lay["m_indices"], n, live=live,
+                          workers=workers)
     y = silu_mul_bf16(G, live)
-    D = bf16_grouped_gemm(y, inp["w2_bf16"], lay["m_indices"], n, live=live)
+    D = bf16_grouped_gemm(y, inp["w2_bf16"], lay["m_indices"], n, live=live,
+                          workers=workers)
     out = gather(D, lay["src2dst"], nv, topk_weights=inp["w"],
                  scale=float(inp.get("routed_scaling_factor", 1.0)))
     lay.update(G=G, y=y, D=D, out=out, live=live, cap=cap)
@@ -304,7 +326,7 @@ def bf16_brute_force(inp, rows=None):
     return out
 
 
-def standard_layer(inp):
+def standard_layer(inp, workers=None):
     """The standard (non-EP) path: `inp` as for `layer` but with x_bf16
     [R, H] (uint16 bf16 bits) in place of x_q / x_s, an optional
     routed_scaling_factor (default 1) and num_valid (default R).  The rows
@@ -316,7 +338,8 @@ def standard_layer(inp):
     inner = {k: v for k, v in inp.items() if k != "x_bf16"}
     inner.update(x_q=x_q, x_s=x_s, num_valid=nv)
     res = layer(inner, mode="post",
-                routed_scaling_factor=float(inp.get("routed_scaling_factor", 1.0)))
+                routed_scaling_factor=float(inp.get("routed_scaling_factor", 1.0)),
+                workers=workers)
     res.update(x_q=x_q, x_s=x_s)
     return res
 

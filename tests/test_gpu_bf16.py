@@ -19,6 +19,8 @@ full, sampled rows against the per-token brute force on host copies of
 their experts.
 """
 
+import os
+
 import numpy as np
 import pytest
 
@@ -143,16 +145,22 @@ def test_bf16_full_size():
     rr = np.nonzero(src >= 0)[0]
     assert np.array_equal(ex[src[src >= 0]], x_bf16[rr])
     print(f"[std_dsv3_bf16] layout bit-exact: total {lay['total']}", flush=True)
+    # 256 sampled rows against the layered oracle restricted to them (the
+    # other rows' slots dropped), on host copies of the experts they touch
     rng = np.random.default_rng(11)
-    rows = np.sort(rng.choice(R, size=4, replace=False))
+    rows = np.sort(rng.choice(R, size=256, replace=False))
     experts = np.unique(d["ids"][rows][d["ids"][rows] >= 0])
     remap = np.full(wl.experts, -1, np.int32)
     remap[experts] = np.arange(len(experts), dtype=np.int32)
-    sub_ids = np.where(d["ids"] >= 0, remap[np.maximum(d["ids"], 0)], -1).astype(np.int32)
+    keep = np.zeros(R, bool)
+    keep[rows] = True
+    sub_ids = np.where((d["ids"] >= 0) & keep[:, None], remap[np.maximum(d["ids"], 0)],
+                       -1).astype(np.int32)
     sel = torch.from_numpy(experts.astype(np.int64)).cuda()
     as_bits = lambda t: t.index_select(0, sel).view(torch.int16).cpu().numpy().view(np.uint16)  # noqa
     o = dict(x_bf16=x_bf16, ids=sub_ids, w=d["w"], num_valid=R, w13_bf16=as_bits(w13),
              w2_bf16=as_bits(w2), align=wl.align, routed_scaling_factor=wl.routed_scale)
-    print(f"[std_dsv3_bf16] oracle on {len(rows)} sampled rows", flush=True)
-    ref = layer.bf16_brute_force(o, rows=rows)
+    print(f"[std_dsv3_bf16] oracle on {len(rows)} sampled rows ({len(experts)} experts)",
+          flush=True)
+    ref = layer.bf16_layer(o, workers=min(16, os.cpu_count() or 1))["out"][rows]
     _check_output(bf16_np(out)[rows], ref, scale=wl.routed_scale)

@@ -13,6 +13,8 @@ Bars (as for the other formats):
 Full size (dsv3_mxfp8): layout bit-exact, sampled rows against the brute force.
 """
 
+import os
+
 import numpy as np
 import pytest
 
@@ -28,7 +30,8 @@ if not torch.cuda.is_available():
     pytest.skip("needs a GPU", allow_module_level=True)
 
 from tests.test_gpu_parity import (_check_output, _oracle_stage_inputs, abs_terms,  # noqa: E402
-                                   bf16_np, check_gemm, check_layout, rows_major, run_gpu)
+                                   bf16_np, check_gemm, check_layout, flipped_rows, rows_major,
+                                   run_gpu)
 
 CASES = [dict(fmt="mxfp8"), dict(fmt="mxfp8", align=16, topk=3, seed=77),
          dict(fmt="mxfp8", rows=200, hidden=512, inter=384, experts=5, global_experts=5,
@@ -90,11 +93,11 @@ def test_mx_full_size():
     inp = make("dsv3_mxfp8")
     mod, out, _ = run_gpu(inp)
     check_layout(mod, inp)
-    R = len(inp["ids"])
-    rng = np.random.default_rng(13)
-    has = np.nonzero((inp["ids"] >= 0).any(axis=1))[0]
-    rows = np.sort(rng.choice(has, size=16, replace=False))
     o = {k: v for k, v in inp.items() if k != "psum_recv_per_rank"}
-    print(f"[dsv3_mxfp8] oracle on {len(rows)} sampled rows", flush=True)
-    ref = layer.brute_force(o, rows=rows)
-    _check_output(bf16_np(out)[rows], ref)
+    print(f"[dsv3_mxfp8] oracle on all {len(inp['ids'])} rows", flush=True)
+    L = layer.layer(o, workers=min(16, os.cpu_count() or 1))
+    got = bf16_np(out)
+    dq = mod.dq[:min(L["total"], mod.capacity)].cpu().numpy()
+    _check_output(got, L["out"], flipped=flipped_rows(L["src2dst"], dq, L["dq"], len(got)),
+                  label="[dsv3_mxfp8]")
+    assert not np.any(got[~(inp["ids"] >= 0).any(axis=1)])    # no local slot -> 0

@@ -22,6 +22,8 @@ bit-exact; the output on sampled rows against the per-token brute force,
 with the weights of just those rows' experts copied to the host.
 """
 
+import os
+
 import numpy as np
 import pytest
 
@@ -36,7 +38,8 @@ pytestmark = pytest.mark.gpu
 if not torch.cuda.is_available():
     pytest.skip("needs a GPU", allow_module_level=True)
 
-from tests.test_gpu_parity import SENT, _check_output, bf16_np, rows_major  # noqa: E402
+from tests.test_gpu_parity import (SENT, _check_output, bf16_np, flipped_rows,  # noqa: E402
+                                   rows_major)
 from tests.test_oracle_standard import std_inputs  # noqa: E402
 
 
@@ -165,13 +168,19 @@ def test_std_full_size():
     assert np.array_equal(exs[dd].view(np.uint8), np.ascontiguousarray(x_s[rr]).view(np.uint8))
     assert np.all(ex[n:] == SENT)
     print(f"[std_dsv3] layout and quantised rows bit-exact: total {n}", flush=True)
-    # sampled rows against the brute force, on host copies of their experts
+    # 256 sampled rows against the layered oracle, on host copies of the
+    # experts they touch; the other rows' slots are dropped (-1) so that the
+    # oracle computes only these rows (each row's result depends only on its
+    # own slots)
     rng = np.random.default_rng(7)
-    rows = np.sort(rng.choice(R, size=4, replace=False))
+    rows = np.sort(rng.choice(R, size=256, replace=False))
     experts = np.unique(d["ids"][rows][d["ids"][rows] >= 0])
     remap = np.full(wl.experts, -1, np.int32)
     remap[experts] = np.arange(len(experts), dtype=np.int32)
-    sub_ids = np.where(d["ids"] >= 0, remap[np.maximum(d["ids"], 0)], -1).astype(np.int32)
+    keep = np.zeros(R, bool)
+    keep[rows] = True
+    sub_ids = np.where((d["ids"] >= 0) & keep[:, None], remap[np.maximum(d["ids"], 0)],
+                       -1).astype(np.int32)
     sel = torch.from_numpy(experts).to(dev)
     o = dict(x_bf16=x_bf16, ids=sub_ids, w=d["w"], num_valid=R,
              w13_q=w13.index_select(0, sel).cpu().numpy(),
@@ -180,5 +189,9 @@ def test_std_full_size():
              w2_s=w2s.index_select(0, sel).cpu().numpy(),
              align=wl.align, fmt=wl.fmt, routed_scaling_factor=wl.routed_scale)
     print(f"[std_dsv3] oracle on {len(rows)} sampled rows ({len(experts)} experts)", flush=True)
-    ref = layer.brute_force(o, rows=rows)
-    _check_output(bf16_np(out)[rows], ref, scale=wl.routed_scale)
+    L = layer.standard_layer(o, workers=min(16, os.cpu_count() or 1))
+    ref = L["out"][rows]
+    flip = flipped_rows(src[rows], mod.dq[:n].cpu().numpy(), L["dq"], len(rows),
+                        src2dst_ref=L["src2dst"][rows])
+    _check_output(bf16_np(out)[rows], ref, scale=wl.routed_scale, flipped=flip,
+                  label="[std_dsv3]")

@@ -97,6 +97,16 @@ def test_silu_mul_closed_form():
     got = layer.silu_mul(g, u)
     assert np.allclose(got, ref, rtol=4e-7, atol=1e-30)
     assert layer.silu_mul(np.float32(0.0), np.float32(3.0)) == 0.0
+    # each of the four float32 operations is one rounding of its exact result:
+    # exp(-g) is the correctly rounded float32 of the float64 exp, then the
+    # add, divide and multiply in IEEE float32 (checked here in float64 with an
+    # explicit rounding after every step)
+    r32 = lambda v: np.asarray(v, np.float64).astype(np.float32).astype(np.float64)  # noqa
+    gg = (np.random.default_rng(4).standard_normal(200_000) * 6).astype(np.float32)
+    uu = np.float32(0.75)
+    e = r32(np.exp(-gg.astype(np.float64)))
+    step = r32(r32(gg.astype(np.float64) / r32(1.0 + e)) * np.float64(uu))
+    assert np.array_equal(layer.silu_mul(gg, uu).astype(np.float64), step)
     # silu is not symmetric in its two inputs
     assert layer.silu_mul(np.float32(-2.0), np.float32(1.0)) != \
         layer.silu_mul(np.float32(1.0), np.float32(-2.0))
