@@ -149,7 +149,9 @@ __device__ __forceinline__ T lds_load(uint32_t addr) {
 // Direct HBM -> LDS loads.  Issued from inline assembly so the compiler does
 // not treat them as LDS writes that every later LDS read must wait for: the
 // kernel orders them itself (vmcnt waits + s_barrier).  Address = 64-bit
-// scalar base + 32-bit per-lane offset; lane i's data lands at lds + i * size.
+// scalar base + 32-bit per-lane offset; lane i's data lands at lds + i * size,
+// the LDS base taken from M0, which the asm names as an input operand so the
+// compiler itself writes it and knows it is in use.
 // A wave-uniform pointer, held in scalar registers (the loads' base operand).
 __device__ __forceinline__ const uint8_t* uniform_ptr(const uint8_t* p) {
   const uint64_t v = (uint64_t)p;
@@ -161,16 +163,12 @@ __device__ __forceinline__ const uint8_t* uniform_ptr(const uint8_t* p) {
 __device__ __forceinline__ void dma16(const uint8_t* base, uint32_t off, uint32_t lds) {
   base = uniform_ptr(base);                   // wave-uniform by construction
   lds = __builtin_amdgcn_readfirstlane(lds);  // M0: wave-uniform by construction
-  asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(off), "s"(base),
-               "s"(lds)
-               : "memory");
+  asm volatile("global_load_lds_dwordx4 %0, %1" ::"v"(off), "s"(base), "{m0}"(lds) : "memory");
 }
 __device__ __forceinline__ void dma4(const uint8_t* base, uint32_t off, uint32_t lds) {
   base = uniform_ptr(base);
   lds = __builtin_amdgcn_readfirstlane(lds);
-  asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dword %0, %1" ::"v"(off), "s"(base),
-               "s"(lds)
-               : "memory");
+  asm volatile("global_load_lds_dword %0, %1" ::"v"(off), "s"(base), "{m0}"(lds) : "memory");
 }
 
 template <int N>
