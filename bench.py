@@ -41,10 +41,11 @@ def parse():
     p.add_argument("--workload", default="dsv3")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-runs", type=int, default=3)
-    p.add_argument("--pmc-target", choices=["gemm", "copy"], default=None,
-                   help="profiling mode: run only this kernel a few times (for rocprofv3 "
-                        "--pmc); 'copy' is a plain 256 MiB device copy used to calibrate "
-                        "the byte counters")
+    p.add_argument("--pmc-target", choices=["gemm", "layer", "copy"], default=None,
+                   help="profiling mode (for rocprofv3 --pmc): 'gemm' runs the layout "
+                        "once and the two GEMMs (with act-quant) three times, 'layer' "
+                        "three whole steps after one warm-up step, 'copy' a plain 256 MiB "
+                        "device copy used to calibrate the byte counters")
     return p.parse_args()
 
 
@@ -332,6 +333,13 @@ def main():
     def stage(i):
         stage_list[i][1]()
 
+    if args.pmc_target == "layer":    # one warm-up step, then 3 whole steps
+        for _ in range(4):
+            for i in range(NS):
+                stage(i)
+        torch.cuda.synchronize()
+        print(json.dumps({"pmc_target": "layer", "status": mod.status.cpu().tolist()}))
+        return
     if args.pmc_target == "gemm":     # layout once, then 3 x (gate_up, act, down)
         stage(0)
         for _ in range(3):

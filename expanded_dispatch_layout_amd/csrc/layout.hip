@@ -8,8 +8,17 @@
 // vLLM PR 54109 PaddedStandard (Motivation/Design: -1 slots, device-side
 // real/padding boundary, zeroed alignment gaps).
 //
-// Three kernels on one stream (two when the block table is small: every
-// scatter workgroup then scans it itself):
+// Small receive buffers (rows * topk <= 65536 slots, rows copied as they
+// are: the DeepSeek-V3-shape share, the padded buffer, the decode share):
+// ONE launch.  Every 1024-thread workgroup reads the whole buffer's valid
+// ids itself (128 KB at the DeepSeek-V3 share, one round trip from L2) and
+// counts, per expert, all of them and those before its own 16-row group
+// (LDS atomics on the few local ids); it then scans the counts into the
+// aligned starts and psum (workgroup 0 writes them and the status) and
+// scatters its group, a wave per row.
+//
+// Larger buffers: up to three kernels on one stream (two when the block
+// table is small: every scatter workgroup then scans it itself):
 //  1. count   a block covers G = 16 16-row groups; its threads read the
 //             block's (row, k) ids coalesced, all loads in flight at once.
 //             Order-free per-expert counts of every group (LDS atomics), then, per
@@ -20,15 +29,20 @@
 //             scan of the aligned counts (every start is aligned, so
 //             start[e] = sum of align(count) over e' < e), psum, total,
 //             flags.
-//  3. scatter one wave per received row.  The stable rank of slot (r, k)
-//             among its expert's slots is its block's offset plus its
-//             group's offset in the block plus the number of that expert's
-//             slots in the earlier rows of the group plus those at k' < k in
-//             row r: two ballots over the group's ids.  Destination =
-//             start[e] + rank; the row (16-byte chunks) and its scales are
-//             read once and written to each destination.  The same grid
-//             zero-fills the alignment pad rows and writes the row labels
-//             (grid-stride), so no extra pass is needed.
+//  3. scatter 768 workgroups, each wave walking received rows grid-stride,
+//             software-pipelined: while one row is stored, the next row's
+//             data and the ids of the row after are in flight.
+// Either way the scatter works the same on a row: the stable rank of slot
+// (r, k) among its expert's slots is its block's (or, fused, the rows
+// before the group's) count plus its group's offset in the block plus the
+// number of that expert's slots in the earlier rows of the group plus those
+// at k' < k in row r: two ballots over the group's ids.  Destination =
+// start[e] + rank; the row (16-byte chunks) and its scales are read once and
+// written to each destination.  The same grid zero-fills the alignment pad
+// rows and writes the row labels (grid-stride), so no extra pass is needed.
+// Rows at or past the valid-row boundary are never read as routing: the
+// scatter (fused or not) does not load their ids, the count kernel ignores
+// the ones it loads with the rest of its block, and their slots get -1.
 //
 // bf16 input (the standard path, SGLang moe_runner/deep_gemm.py source,
 // pre_permute_standard_to_deep_gemm: per-token-group quantisation, then the
@@ -43,6 +57,7 @@
 // shape [1, 32], UE8M0 scales): the received scales are one byte per 1x32
 // group; the scatter copies each 128-wide block's four bytes as one 4-byte
 // word, K-block-major like the other formats' scales.
+#include <algorithm>
 #include <mutex>
 
 #include "common.hpp"
@@ -54,11 +69,12 @@ constexpr int kGroupRows = 16;      // rows per counted group
 constexpr int kCountThreads = 256;  // one row per thread: 16 groups per block
 constexpr int kScanThreads = 1024;
 constexpr int kScatterThreads = 256;
-constexpr int kRowsPerScatterBlock = kScatterThreads / 64;
+constexpr int kFusedThreads = 1024;  // fused layout: a wave per row of a 16-row group
 
 // Groups per count block (the [groups][E] count table stays in LDS).
 __host__ __device__ inline int groups_per_block(int) { return kCountThreads / kGroupRows; }
 constexpr int kFoldScanInts = 4096;  // block table size up to which the scatter scans it
+constexpr int64_t kFusedSlots = 65536;  // receive-buffer slots up to which no count kernel runs
 
 struct Workspace {
   int32_t* grp;       // [ngroups][E]: offset of each group within its block
@@ -239,22 +255,24 @@ __device__ __forceinline__ int last_le(const int32_t* a, int n, int v) {
   return lo;
 }
 
-// Exclusive scan over a 256-thread workgroup of n <= 1024 values held as
-// v[i] (i < n); each thread owns a contiguous run of up to four.  Writes the
-// exclusive prefixes to out[i] and returns the total (all threads).
-__device__ int block_excl_scan_256(const int* v, int* out, int n, int* lds4) {
+// Exclusive scan over a workgroup of NTH threads of n <= 1024 values held as
+// v[i] (i < n); each thread owns a contiguous run of them.  Writes the
+// exclusive prefixes to out[i] and returns the total (all threads).  lds_w:
+// NTH / 64 ints of scratch.
+template <int NTH>
+__device__ int block_excl_scan_n(const int* v, int* out, int n, int* lds_w) {
   const int t = threadIdx.x, lane = t & 63, wid = t >> 6;
-  const int per = (n + kScatterThreads - 1) / kScatterThreads;
+  const int per = (n + NTH - 1) / NTH;
   const int lo = min(n, t * per), hi = min(n, lo + per);
   int sum = 0;
   for (int i = lo; i < hi; ++i) sum += v[i];
   const int incl = wave_incl_scan_i(sum);
-  if (lane == 63) lds4[wid] = incl;
+  if (lane == 63) lds_w[wid] = incl;
   __syncthreads();
   int base = 0, total = 0;
-  for (int w = 0; w < kScatterThreads / 64; ++w) {
-    if (w < wid) base += lds4[w];
-    total += lds4[w];
+  for (int w = 0; w < NTH / 64; ++w) {
+    if (w < wid) base += lds_w[w];
+    total += lds_w[w];
   }
   int run = base + incl - sum;
   for (int i = lo; i < hi; ++i) {
@@ -266,51 +284,50 @@ __device__ int block_excl_scan_256(const int* v, int* out, int n, int* lds4) {
 }
 
 // Ids of row r's group predecessors (up to 15 * topk <= 480 values, eight
-// per lane; -1 past them) and, in lane k < topk, of slot (r, k).
-__device__ __forceinline__ void load_row_ids(const int32_t* __restrict__ ids, int64_t r, int topk,
-                                             int lane, int* prev, int& myid) {
-  const int64_t g_first = r / kGroupRows * kGroupRows;
-  const int nprev = (int)(r - g_first) * topk;
-#pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    const int idx = i * 64 + lane;
-    prev[i] = idx < nprev ? ids[g_first * topk + idx] : -1;
-  }
-  myid = lane < topk ? ids[r * topk + lane] : -1;
-}
-
-// One received row's wave-level state: its ids, which of its slots are
-// local, and (for a row with a local slot) the loads that do not depend on
-// the destinations: the row's first 8 KB, its first 64 scales, each local
-// slot's weight and its group's offset within its block.
-struct RowFetch {
+// per lane; -1 past them) and, in lane k < topk, of slot (r, k).  Rows at or
+// past the valid boundary route nowhere and are not read (a valid row's
+// group predecessors are valid too).
+struct RowIds {
   int prev[8];
   int myid;
-  bool mine;
-  uint64_t live;
+
+  __device__ __forceinline__ void load(const int32_t* __restrict__ ids, int64_t r, int64_t nv,
+                                       int topk, int lane) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) prev[i] = -1;
+    myid = -1;
+    if (r >= nv) return;
+    const int64_t g_first = r / kGroupRows * kGroupRows;
+    const int nprev = (int)(r - g_first) * topk;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int idx = i * 64 + lane;
+      if (idx < nprev) prev[i] = ids[g_first * topk + idx];
+    }
+    if (lane < topk) myid = ids[r * topk + lane];
+  }
+};
+
+// The loads of a row with a local slot that do not depend on the
+// destinations: its first 8 KB, its first 64 scales, each local slot's
+// weight and its group's offset within its block.
+struct RowData {
   u32x4 v[8];
   float sf;
   uint8_t sb;
   float wt;
   int grp;
 
-  __device__ __forceinline__ void ids_of(const int32_t* __restrict__ ids, int64_t r, int64_t nv,
-                                         int topk, int E, int lane) {
-    load_row_ids(ids, r, topk, lane, prev, myid);
-    // Rows past the valid boundary route nowhere.  A valid row's group
-    // predecessors are valid too, so prev needs no such check.
-    if (r >= nv) myid = -1;
-    mine = myid >= 0 && myid < E;
-    live = __ballot(mine);
-  }
-  // kQ: the row is bf16 (2 bytes per element) and has no scales.
+  // kQ: the row is bf16 (2 bytes per element) and has no scales.  mine: this
+  // lane's slot is local (lane k < topk holds slot k).
   template <bool kQ>
-  __device__ __forceinline__ void data_of(const uint8_t* __restrict__ x, int64_t x_stride,
-                                          const uint8_t* __restrict__ x_scale,
-                                          int64_t x_scale_stride_bytes, int scale_bytes,
-                                          const float* __restrict__ topk_w,
-                                          const int32_t* __restrict__ grp_off, bool weights,
-                                          int64_t r, int hidden, int topk, int E, int lane) {
+  __device__ __forceinline__ void load(const uint8_t* __restrict__ x, int64_t x_stride,
+                                       const uint8_t* __restrict__ x_scale,
+                                       int64_t x_scale_stride_bytes, int scale_bytes,
+                                       const float* __restrict__ topk_w,
+                                       const int32_t* __restrict__ grp_off, bool weights,
+                                       int64_t r, int hidden, int topk, int E, int lane,
+                                       bool mine, int myid) {
     const int nch = kQ ? hidden / 8 : hidden / 16, nsc = hidden / kGroup;
     const u32x4* src = reinterpret_cast<const u32x4*>(x + r * x_stride);
     const uint8_t* srow = x_scale + r * x_scale_stride_bytes;
@@ -329,7 +346,7 @@ struct RowFetch {
     grp = 0;
     if (mine) {
       if (weights) wt = topk_w[r * topk + lane];
-      grp = grp_off[(r / kGroupRows) * E + myid];
+      if (grp_off) grp = grp_off[(r / kGroupRows) * E + myid];
     }
   }
 };
@@ -379,10 +396,58 @@ __device__ __forceinline__ void quant_pass(const u32x4 (&v)[8], int c0, int nch,
   }
 }
 
+// Count of the valid slots with local ids, per expert, over the whole
+// receive buffer (into tot) and over the slots before `npre` (into pre):
+// every workgroup of the fused launch runs this itself.  ids are read as
+// 16-byte vectors when aligned (four slots each), eight in flight per
+// thread; only local ids touch LDS (one atomic add each).
+template <int NTH>
+__device__ __forceinline__ void count_all(const int32_t* __restrict__ ids, int64_t nslot,
+                                          int64_t npre, int E, bool vec, int32_t* tot,
+                                          int32_t* pre, int& bad) {
+  const int t = threadIdx.x;
+  auto one = [&](int id, int64_t s) __attribute__((always_inline)) {
+    if (id >= E) bad = 1;
+    else if (id >= 0) {
+      atomicAdd(&tot[id], 1);
+      if (s < npre) atomicAdd(&pre[id], 1);
+    }
+  };
+  int64_t done = 0;
+  if (vec) {
+    const int64_t n4 = nslot >> 2;
+    const int4* ids4 = reinterpret_cast<const int4*>(ids);
+    constexpr int U = 8;
+    for (int64_t i0 = 0; i0 < n4; i0 += (int64_t)U * NTH) {
+      int4 v[U];
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int64_t i = i0 + u * NTH + t;
+        v[u] = i < n4 ? ids4[i] : make_int4(-1, -1, -1, -1);
+      }
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int64_t s = (i0 + u * NTH + t) * 4;
+        one(v[u].x, s);
+        one(v[u].y, s + 1);
+        one(v[u].z, s + 2);
+        one(v[u].w, s + 3);
+      }
+    }
+    done = n4 * 4;
+  }
+  for (int64_t s = done + t; s < nslot; s += NTH) one(ids[s], s);
+}
+
 // kQ: bf16 input rows quantised here (x_scale unused), with UE8M0 scales
 // when kQU8 (else fp32); otherwise fp8 rows and their scales are copied.
-template <bool kQ, bool kQU8>
-__global__ __launch_bounds__(kScatterThreads) void expand_scatter_kernel(
+// kFused: no count kernel ran; every workgroup counts the whole buffer's
+// valid slots itself (count_all) and owns one 16-row group (rows
+// 16 * blockIdx.x ..), wave w its rows w, w + 4, w + 8, w + 12.  Otherwise
+// the count kernel's tables are used (with `fold`, the block table is
+// scanned here by every workgroup) and the waves walk the rows grid-stride.
+template <bool kQ, bool kQU8, bool kFused>
+__global__ __launch_bounds__(kFused ? kFusedThreads : kScatterThreads) void expand_scatter_kernel(
     const uint8_t* __restrict__ x, int64_t x_stride, const uint8_t* __restrict__ x_scale,
     int64_t x_scale_stride_bytes, int scale_bytes, const int32_t* __restrict__ ids,
     const float* __restrict__ topk_w, const int32_t* __restrict__ psum_rank, int nsrc,
@@ -391,94 +456,109 @@ __global__ __launch_bounds__(kScatterThreads) void expand_scatter_kernel(
     const int32_t* __restrict__ blk_flag, int fold, const int32_t* __restrict__ starts_g,
     const int32_t* __restrict__ padbase_g, int32_t* __restrict__ psum_g,
     int32_t* __restrict__ status, uint8_t* __restrict__ ex, uint8_t* __restrict__ ex_scale,
-    int32_t* __restrict__ m_indices, int32_t* __restrict__ src2dst, float* __restrict__ row_weight) {
+    int32_t* __restrict__ m_indices, int32_t* __restrict__ src2dst, float* __restrict__ row_weight,
+    int ids_vec) {
+  constexpr int NT = kFused ? kFusedThreads : kScatterThreads;
   extern __shared__ int32_t lds[];
   int32_t* l_starts = lds;                // [E]
   int32_t* l_padbase = l_starts + E;      // [E + 1]
   int32_t* l_psum = l_padbase + E + 1;    // [E]
   int32_t* l_tmp = l_psum + E;            // [E]
-  int32_t* l_blk = l_tmp + E;             // [nblk][E] (fold)
-  __shared__ int lds4[4];
+  int32_t* l_blk = l_tmp + E;             // fold: [nblk][E]; fused: [E] (rows before the group)
+  __shared__ int lds_w[NT / 64];
   __shared__ int l_total, l_flag;
   const int t = threadIdx.x, lane = t & 63, wid = t >> 6;
-  const int64_t gwaves = (int64_t)gridDim.x * (kScatterThreads / 64);
-  const int64_t wave0 = (int64_t)blockIdx.x * (kScatterThreads / 64) + wid;
-  // The first row's loads do not depend on the scan below: issue them
-  // first (ids, then the row's data if it has a local slot), so that the
-  // scan runs while they are in flight.
-  // The count kernel's block table (its first 256 entries, which is all of
-  // it for the DeepSeek-V3-shape share) is read before anything waits, so
-  // its round trip overlaps the ids'.
+  const int64_t gwaves = (int64_t)gridDim.x * (NT / 64);
+  const int64_t wave0 = (int64_t)blockIdx.x * (NT / 64) + wid;
+  const int64_t nv = valid_rows(psum_rank, nsrc, rows);
+  // This wave's rows: [r_first, r_end) in steps of r_step.
+  const int64_t g0 = kFused ? (int64_t)blockIdx.x * kGroupRows : 0;
+  const int64_t r_first = kFused ? g0 + wid : wave0;
+  const int64_t r_end = kFused ? min(g0 + kGroupRows, rows) : rows;
+  const int64_t r_step = kFused ? NT / 64 : gwaves;
+  const bool weights = row_weight != nullptr;
+  const int32_t* grp_tab = kFused ? nullptr : grp_off;
+
+  // The first row's ids (and, fold, the first 256 entries of the count
+  // kernel's block table, which is all of it at the DeepSeek-V3 share) are
+  // requested before anything waits.
   const int nbe = fold ? nblk * E : 0;
   const int blk0 = t < nbe ? blk_g[t] : 0;
   const int flg0 = (fold && t < nblk) ? blk_flag[t] : 0;
-  const int64_t nv = valid_rows(psum_rank, nsrc, rows);
-  RowFetch f;
-  if (wave0 < rows) f.ids_of(ids, wave0, nv, topk, E, lane);
-  // Stored now: its load was issued before the ids', so waiting for it here
-  // costs nothing, whereas after the row's loads the wait would cover them.
+  RowIds ia;
+  if (r_first < r_end) ia.load(ids, r_first, nv, topk, lane);
   if (t < nbe) l_blk[t] = blk0;
-  if (wave0 < rows && f.live)
-    f.data_of<kQ>(x, x_stride, x_scale, x_scale_stride_bytes, scale_bytes, topk_w, grp_off,
-                  row_weight != nullptr, wave0, hidden, topk, E, lane);
-  const int32_t* blk_off;  // exclusive per-block offsets, [nblk][E]
-  if (fold) {
-    // The scan over the (few) block totals, done by every workgroup: block
-    // offsets per expert, expert totals, aligned starts, pad prefix.
-    for (int i = t + kScatterThreads; i < nbe; i += kScatterThreads) l_blk[i] = blk_g[i];
-    int fl = flg0;
-    for (int b = t + kScatterThreads; b < nblk; b += kScatterThreads) fl |= blk_flag[b];
+  const int32_t* blk_off;  // per-expert offset of a row's group: [nblk][E] or [E]
+  if (kFused || fold) {
     if (t == 0) l_flag = 0;
-    __syncthreads();
-    if (fl) atomicOr(&l_flag, fl);
-    if (nblk <= 8 || E >= 64) {  // a thread per expert walks the blocks in order
-      for (int e = t; e < E; e += kScatterThreads) {
-        int run = 0;
-        for (int b = 0; b < nblk; ++b) {
-          const int c = l_blk[b * E + e];
-          l_blk[b * E + e] = run;
-          run += c;
-        }
-        l_psum[e] = run;  // the count, for now
+    int fl = 0;
+    if constexpr (kFused) {
+      for (int e = t; e < E; e += NT) {
+        l_psum[e] = 0;  // totals
+        l_blk[e] = 0;   // counts before this group
       }
-    } else {  // a wave per expert scans 64 blocks at a time
-      for (int e = wid; e < E; e += kScatterThreads / 64) {
-        int carry = 0;
-        for (int b0 = 0; b0 < nblk; b0 += 64) {
-          const int b = b0 + lane;
-          const int c = b < nblk ? l_blk[b * E + e] : 0;
-          const int incl = wave_incl_scan_i(c);
-          if (b < nblk) l_blk[b * E + e] = carry + incl - c;
-          carry += __shfl(incl, 63, 64);
-        }
-        if (lane == 0) l_psum[e] = carry;
-      }
+      __syncthreads();
+      count_all<NT>(ids, nv * topk, min(g0, nv) * topk, E, ids_vec != 0, l_psum, l_blk, fl);
+      fl = fl ? MOE_FLAG_EXPERT_ID_RANGE : 0;
+    } else {
+      // The scan over the (few) block totals, done by every workgroup: block
+      // offsets per expert, expert totals, aligned starts, pad prefix.
+      for (int i = t + NT; i < nbe; i += NT) l_blk[i] = blk_g[i];
+      fl = flg0;
+      for (int b = t + NT; b < nblk; b += NT) fl |= blk_flag[b];
     }
     __syncthreads();
+    if (fl) atomicOr(&l_flag, fl);
+    if constexpr (!kFused) {
+      if (nblk <= 8 || E >= 64) {  // a thread per expert walks the blocks in order
+        for (int e = t; e < E; e += NT) {
+          int run = 0;
+          for (int b = 0; b < nblk; ++b) {
+            const int c = l_blk[b * E + e];
+            l_blk[b * E + e] = run;
+            run += c;
+          }
+          l_psum[e] = run;  // the count, for now
+        }
+      } else {  // a wave per expert scans 64 blocks at a time
+        for (int e = wid; e < E; e += NT / 64) {
+          int carry = 0;
+          for (int b0 = 0; b0 < nblk; b0 += 64) {
+            const int b = b0 + lane;
+            const int c = b < nblk ? l_blk[b * E + e] : 0;
+            const int incl = wave_incl_scan_i(c);
+            if (b < nblk) l_blk[b * E + e] = carry + incl - c;
+            carry += __shfl(incl, 63, 64);
+          }
+          if (lane == 0) l_psum[e] = carry;
+        }
+      }
+      __syncthreads();
+    }
     if (E <= 64) {  // one wave: aligned starts, pad prefix, psum, total
       if (wid == 0) {
         const int c = lane < E ? l_psum[lane] : 0;
         const int al = align_up_i(c, align);
-        const int ia = wave_incl_scan_i(al);
+        const int ia_ = wave_incl_scan_i(al);
         const int ip = wave_incl_scan_i(al - c);
         if (lane < E) {
-          l_starts[lane] = ia - al;
+          l_starts[lane] = ia_ - al;
           l_padbase[lane] = ip - (al - c);
-          l_psum[lane] = ia - al + c;
+          l_psum[lane] = ia_ - al + c;
         }
         if (lane == 63) {
           l_padbase[E] = ip;
-          l_total = ia;
+          l_total = ia_;
         }
       }
     } else {
-      for (int e = t; e < E; e += kScatterThreads) l_tmp[e] = align_up_i(l_psum[e], align);
+      for (int e = t; e < E; e += NT) l_tmp[e] = align_up_i(l_psum[e], align);
       __syncthreads();
-      const int total = block_excl_scan_256(l_tmp, l_starts, E, lds4);
-      for (int e = t; e < E; e += kScatterThreads) l_tmp[e] -= l_psum[e];  // pad rows
+      const int total = block_excl_scan_n<NT>(l_tmp, l_starts, E, lds_w);
+      for (int e = t; e < E; e += NT) l_tmp[e] -= l_psum[e];  // pad rows
       __syncthreads();
-      const int padtot = block_excl_scan_256(l_tmp, l_padbase, E, lds4);
-      for (int e = t; e < E; e += kScatterThreads) l_psum[e] += l_starts[e];
+      const int padtot = block_excl_scan_n<NT>(l_tmp, l_padbase, E, lds_w);
+      for (int e = t; e < E; e += NT) l_psum[e] += l_starts[e];
       if (t == 0) {
         l_padbase[E] = padtot;
         l_total = total;
@@ -487,7 +567,7 @@ __global__ __launch_bounds__(kScatterThreads) void expand_scatter_kernel(
     __syncthreads();
     const int total = l_total;
     if (blockIdx.x == 0) {  // the layout's outputs
-      for (int e = t; e < E; e += kScatterThreads) psum_g[e] = l_psum[e];
+      for (int e = t; e < E; e += NT) psum_g[e] = l_psum[e];
       if (t == 0) {
         status[0] = total;
         status[1] = l_flag | (total > capacity ? MOE_FLAG_CAPACITY_OVERFLOW : 0);
@@ -495,11 +575,11 @@ __global__ __launch_bounds__(kScatterThreads) void expand_scatter_kernel(
     }
     blk_off = l_blk;
   } else {
-    for (int i = t; i < E; i += kScatterThreads) {
+    for (int i = t; i < E; i += NT) {
       l_starts[i] = starts_g[i];
       l_psum[i] = psum_g[i];
     }
-    for (int i = t; i <= E; i += kScatterThreads) l_padbase[i] = padbase_g[i];
+    for (int i = t; i <= E; i += NT) l_padbase[i] = padbase_g[i];
     if (t == 0) l_total = status[0];
     __syncthreads();
     blk_off = blk_g;
@@ -510,111 +590,142 @@ __global__ __launch_bounds__(kScatterThreads) void expand_scatter_kernel(
   const int nch = hidden / 16;                     // 16-byte chunks of an expanded row
   const int nch_in = kQ ? hidden / 8 : nch;        // ... of a received row
 
-  // ---- one wave per received row ----
-  for (int64_t r = wave0; r < rows; r += gwaves) {
-    if (r != wave0) {
-      f.ids_of(ids, r, nv, topk, E, lane);
-      if (f.live)
-        f.data_of<kQ>(x, x_stride, x_scale, x_scale_stride_bytes, scale_bytes, topk_w, grp_off,
-                      row_weight != nullptr, r, hidden, topk, E, lane);
+  // ---- the wave's rows, software-pipelined: while row r is stored, the
+  // data of the next row and the ids of the row after are in flight ----
+  RowData da;
+  bool mine_a = ia.myid >= 0 && ia.myid < E;
+  uint64_t live_a = __ballot(mine_a);
+  if (r_first < r_end && live_a)
+    da.load<kQ>(x, x_stride, x_scale, x_scale_stride_bytes, scale_bytes, topk_w, grp_tab, weights,
+                r_first, hidden, topk, E, lane, mine_a, ia.myid);
+  RowIds ib;  // (fused: each wave has one row, nothing to prefetch)
+  if (!kFused && r_first + r_step < r_end) ib.load(ids, r_first + r_step, nv, topk, lane);
+  for (int64_t r = r_first; r < r_end; r += r_step) {
+    // next row's data (its ids have been in flight since the last row), and
+    // the ids of the row after it
+    // (ids first: the next iteration waits for them while this data may
+    // still be in flight, loads completing in order)
+    const int64_t rn = r + r_step;
+    bool mine_b = false;
+    uint64_t live_b = 0ull;
+    RowIds ic;
+    RowData db;
+    if constexpr (!kFused) {
+      mine_b = ib.myid >= 0 && ib.myid < E;
+      live_b = rn < r_end ? __ballot(mine_b) : 0ull;
+      if (rn + r_step < r_end) ic.load(ids, rn + r_step, nv, topk, lane);
+      if (live_b)
+        db.load<kQ>(x, x_stride, x_scale, x_scale_stride_bytes, scale_bytes, topk_w, grp_tab,
+                    weights, rn, hidden, topk, E, lane, mine_b, ib.myid);
     }
-    if (f.live == 0) {
+
+    if (live_a == 0) {
       if (lane < topk) src2dst[r * topk + lane] = -1;
-      continue;
-    }
-    const int64_t g = r / kGroupRows;
-    // Stable rank of each live slot among its expert's slots of the group:
-    // earlier rows' slots, then this row's slots at smaller k.
-    int rank = 0;
-    for (uint64_t mm = f.live; mm; mm &= mm - 1) {
-      const int k = __builtin_ctzll(mm);
-      const int e = __shfl(f.myid, k, 64);
-      int rk = __popcll(__ballot(f.myid == e) & ((1ull << k) - 1ull));
+    } else {
+      const int64_t g = r / kGroupRows;
+      // Stable rank of each live slot among its expert's slots of the group:
+      // earlier rows' slots, then this row's slots at smaller k.
+      int rank = 0;
+      for (uint64_t mm = live_a; mm; mm &= mm - 1) {
+        const int k = __builtin_ctzll(mm);
+        const int e = __shfl(ia.myid, k, 64);
+        int rk = __popcll(__ballot(ia.myid == e) & ((1ull << k) - 1ull));
 #pragma unroll
-      for (int i = 0; i < 8; ++i) rk += __popcll(__ballot(f.prev[i] == e));
-      if (lane == k) rank = rk;
-    }
-    int d = -1;
-    if (f.mine) {
-      const int64_t dd =
-          (int64_t)l_starts[f.myid] + blk_off[(g / G) * E + f.myid] + f.grp + rank;
-      if (dd < capacity) {
-        d = (int)dd;
-        if (row_weight) row_weight[d] = f.wt;
+        for (int i = 0; i < 8; ++i) rk += __popcll(__ballot(ia.prev[i] == e));
+        if (lane == k) rank = rk;
       }
-    }
-    if (lane < topk) src2dst[r * topk + lane] = d;
-    const uint64_t mask = __ballot(d >= 0);
-    if (mask == 0) continue;
-    const u32x4* src = reinterpret_cast<const u32x4*>(x + r * x_stride);
-    const uint8_t* srow = x_scale + r * x_scale_stride_bytes;
-    for (int c0 = 0; c0 < nch_in; c0 += 64 * 8) {
-      if (c0 > 0) {
-#pragma unroll
-        for (int u = 0; u < 8; ++u) {
-          const int c = c0 + u * 64 + lane;
-          if (c < nch_in) f.v[u] = src[c];
+      int d = -1;
+      if (mine_a) {
+        const int64_t off = kFused ? (int64_t)blk_off[ia.myid]
+                                   : (int64_t)blk_off[(g / G) * E + ia.myid] + da.grp;
+        const int64_t dd = (int64_t)l_starts[ia.myid] + off + rank;
+        if (dd < capacity) {
+          d = (int)dd;
+          if (weights) row_weight[d] = da.wt;
         }
       }
-      if constexpr (kQ) {
-        // Quantise the pass once, then store it to every destination: the
-        // codes of chunk c at byte 8c of the expanded row, the scale of group
-        // c / 16 (K-block-major) from the group's first lane.
-        uint2 q[8];
-        uint32_t sc[8];
-        quant_pass<kQU8>(f.v, c0, nch_in, lane, q, sc);
-        for (uint64_t mm = mask; mm; mm &= mm - 1) {
-          const int dk = __shfl(d, __builtin_ctzll(mm), 64);
-          uint2* dst = reinterpret_cast<uint2*>(ex + (int64_t)dk * hidden);
+      if (lane < topk) src2dst[r * topk + lane] = d;
+      const uint64_t mask = __ballot(d >= 0);
+      if (mask != 0) {
+        const u32x4* src = reinterpret_cast<const u32x4*>(x + r * x_stride);
+        const uint8_t* srow = x_scale + r * x_scale_stride_bytes;
+        for (int c0 = 0; c0 < nch_in; c0 += 64 * 8) {
+          if (c0 > 0) {
 #pragma unroll
-          for (int u = 0; u < 8; ++u) {
-            const int c = c0 + u * 64 + lane;
-            if (c < nch_in) {
-              dst[c] = q[u];
-              if ((lane & 15) == 0) {
-                const int64_t at = (int64_t)(c >> 4) * capacity + dk;
-                if (kQU8) ex_scale[at] = (uint8_t)sc[u];
-                else reinterpret_cast<uint32_t*>(ex_scale)[at] = sc[u];
+            for (int u = 0; u < 8; ++u) {
+              const int c = c0 + u * 64 + lane;
+              if (c < nch_in) da.v[u] = src[c];
+            }
+          }
+          if constexpr (kQ) {
+            // Quantise the pass once, then store it to every destination: the
+            // codes of chunk c at byte 8c of the expanded row, the scale of
+            // group c / 16 (K-block-major) from the group's first lane.
+            uint2 q[8];
+            uint32_t sc[8];
+            quant_pass<kQU8>(da.v, c0, nch_in, lane, q, sc);
+            for (uint64_t mm = mask; mm; mm &= mm - 1) {
+              const int dk = __shfl(d, __builtin_ctzll(mm), 64);
+              uint2* dst = reinterpret_cast<uint2*>(ex + (int64_t)dk * hidden);
+#pragma unroll
+              for (int u = 0; u < 8; ++u) {
+                const int c = c0 + u * 64 + lane;
+                if (c < nch_in) {
+                  dst[c] = q[u];
+                  if ((lane & 15) == 0) {
+                    const int64_t at = (int64_t)(c >> 4) * capacity + dk;
+                    if (kQU8) ex_scale[at] = (uint8_t)sc[u];
+                    else reinterpret_cast<uint32_t*>(ex_scale)[at] = sc[u];
+                  }
+                }
+              }
+            }
+          } else {
+            for (uint64_t mm = mask; mm; mm &= mm - 1) {
+              const int dk = __shfl(d, __builtin_ctzll(mm), 64);
+              u32x4* dst = reinterpret_cast<u32x4*>(ex + (int64_t)dk * hidden);
+#pragma unroll
+              for (int u = 0; u < 8; ++u) {
+                const int c = c0 + u * 64 + lane;
+                if (c < nch) dst[c] = da.v[u];
               }
             }
           }
         }
-        continue;
-      }
-      for (uint64_t mm = mask; mm; mm &= mm - 1) {
-        const int dk = __shfl(d, __builtin_ctzll(mm), 64);
-        u32x4* dst = reinterpret_cast<u32x4*>(ex + (int64_t)dk * hidden);
-#pragma unroll
-        for (int u = 0; u < 8; ++u) {
-          const int c = c0 + u * 64 + lane;
-          if (c < nch) dst[c] = f.v[u];
+        if constexpr (!kQ) {
+          // Scales: the shuffles run with every lane active (a lane-divergent
+          // shuffle could read an inactive lane), the stores only where c < nsc.
+          for (int c0 = 0; c0 < nsc; c0 += 64) {
+            const int c = c0 + lane;
+            if (c0 > 0 && c < nsc) {
+              if (scale_bytes == 4) da.sf = reinterpret_cast<const float*>(srow)[c];
+              else da.sb = srow[c];
+            }
+            // ex_scale is K-block-major: scale (row dk, block c) at c * capacity + dk.
+            for (uint64_t mm = mask; mm; mm &= mm - 1) {
+              const int dk = __shfl(d, __builtin_ctzll(mm), 64);
+              if (c < nsc) {
+                const int64_t at = (int64_t)c * capacity + dk;
+                if (scale_bytes == 4) reinterpret_cast<float*>(ex_scale)[at] = da.sf;
+                else ex_scale[at] = da.sb;
+              }
+            }
+          }
         }
       }
     }
-    if constexpr (kQ) continue;  // the scales were written with the codes
-    // Scales: the shuffles run with every lane active (a lane-divergent
-    // shuffle could read an inactive lane), the stores only where c < nsc.
-    for (int c0 = 0; c0 < nsc; c0 += 64) {
-      const int c = c0 + lane;
-      if (c0 > 0 && c < nsc) {
-        if (scale_bytes == 4) f.sf = reinterpret_cast<const float*>(srow)[c];
-        else f.sb = srow[c];
-      }
-      // ex_scale is K-block-major: scale (row dk, block c) at c * capacity + dk.
-      for (uint64_t mm = mask; mm; mm &= mm - 1) {
-        const int dk = __shfl(d, __builtin_ctzll(mm), 64);
-        if (c < nsc) {
-          const int64_t at = (int64_t)c * capacity + dk;
-          if (scale_bytes == 4) reinterpret_cast<float*>(ex_scale)[at] = f.sf;
-          else ex_scale[at] = f.sb;
-        }
-      }
+    if constexpr (!kFused) {  // rotate the pipeline
+      ia = ib;
+      ib = ic;
+      da = db;
+      mine_a = mine_b;
+      live_a = live_b;
     }
   }
 
   // ---- grid-stride: row labels and alignment pad rows ----
-  const int64_t gthreads = (int64_t)gridDim.x * kScatterThreads;
-  const int64_t gtid = (int64_t)blockIdx.x * kScatterThreads + t;
+  const int64_t gthreads = (int64_t)gridDim.x * NT;
+  const int64_t gtid = (int64_t)blockIdx.x * NT + t;
   for (int64_t i = gtid; i < capacity; i += gthreads) {
     int lab = -1;
     if (i < nrows_ex) lab = last_le(l_starts, E, (int)i);
@@ -704,42 +815,57 @@ moe_status expand_layout(bool bf16, const void* x, int64_t x_stride, const void*
 
   const int G = groups_per_block(E);
   const int64_t nb = num_blocks(rows, E);
-  // Small block table: every scatter workgroup scans it itself (no scan
-  // kernel); otherwise the scan kernel does it once.
-  const bool fold = nb * E <= kFoldScanInts;
-  {
-  if (ng > 0) {
-    const size_t lds = size_t(G) * E * 4;
-    hipLaunchKernelGGL(expand_count_kernel, dim3((unsigned)nb), dim3(kCountThreads), lds, s,
-                       topk_ids, psum_recv_per_rank, num_src_ranks, rows, topk, E, G, ng, w.grp,
-                       w.blk, w.blk_flag);
-    if (hipGetLastError() != hipSuccess) return MOE_ERR_LAUNCH;
+  // Small receive buffers: no count kernel; every scatter workgroup (1024
+  // threads) counts the whole buffer's valid slots itself (at most
+  // kFusedSlots ids, one round trip from L2) and owns one 16-row group, a
+  // wave per row: one launch for the whole layout.
+  const bool fused = rows * topk <= kFusedSlots && !(bf16 && !keep);  // (quantising: registers)
+  // Otherwise: count kernel; a small block table is scanned by every scatter
+  // workgroup itself (no scan kernel), a large one by the scan kernel once.
+  const bool fold = !fused && nb * E <= kFoldScanInts;
+  if (!fused) {
+    if (ng > 0) {
+      const size_t lds = size_t(G) * E * 4;
+      hipLaunchKernelGGL(expand_count_kernel, dim3((unsigned)nb), dim3(kCountThreads), lds, s,
+                         topk_ids, psum_recv_per_rank, num_src_ranks, rows, topk, E, G, ng,
+                         w.grp, w.blk, w.blk_flag);
+      if (hipGetLastError() != hipSuccess) return MOE_ERR_LAUNCH;
+    }
+    if (!fold) {
+      hipLaunchKernelGGL(expand_scan_kernel, dim3(1), dim3(kScanThreads), 0, s, w.blk,
+                         w.blk_flag, nb, E, align, capacity, w.starts, w.padbase, psum, status);
+      if (hipGetLastError() != hipSuccess) return MOE_ERR_LAUNCH;
+    }
   }
-  if (!fold) {
-    hipLaunchKernelGGL(expand_scan_kernel, dim3(1), dim3(kScanThreads), 0, s, w.blk,
-                       w.blk_flag, nb, E, align, capacity, w.starts, w.padbase, psum, status);
-    if (hipGetLastError() != hipSuccess) return MOE_ERR_LAUNCH;
+  // Fused: a workgroup per 16-row group (at least one, which writes the
+  // psum and the status).  Otherwise 768 workgroups (three per CU, what the
+  // kernel's registers allow to be resident at once), each wave walking rows
+  // grid-stride with the next row in flight; either way enough workgroups
+  // that the label fill and the pad zeroing spread over the chip.
+  const int64_t grid = fused ? std::max<int64_t>(1, (rows + kGroupRows - 1) / kGroupRows)
+                             : 768;
+  const size_t lds = (size_t(4) * E + 1 + (fused ? size_t(E) : fold ? size_t(nb) * E : 0)) * 4;
+  const int hdim = keep ? 2 * hidden : hidden;
+  const int64_t sstride = mx ? x_scale_stride : x_scale_stride * scale_bytes;
+  const int ids_vec = ((uintptr_t)topk_ids % 16) == 0;
+  const bool q = bf16 && !keep, qu8 = q && fmt == MOE_SCALE_UE8M0;
+#define MOE_SCATTER_ARGS                                                                      \
+  (const uint8_t*)x, x_stride, (const uint8_t*)x_scale, sstride, scale_bytes, topk_ids,        \
+      topk_weights, psum_recv_per_rank, num_src_ranks, rows, hdim, topk, E, capacity, align,   \
+      w.grp, w.blk, G, (int)nb, w.blk_flag, fold ? 1 : 0, w.starts, w.padbase, psum, status,   \
+      (uint8_t*)ex, (uint8_t*)ex_scale, m_indices, src2dst, row_weight, ids_vec
+  if (fused) {
+    auto k = !q ? expand_scatter_kernel<false, false, true>
+             : qu8 ? expand_scatter_kernel<true, true, true>
+                   : expand_scatter_kernel<true, false, true>;
+    hipLaunchKernelGGL(k, dim3((unsigned)grid), dim3(kFusedThreads), lds, s, MOE_SCATTER_ARGS);
+  } else {
+    auto k = !q ? expand_scatter_kernel<false, false, false>
+             : qu8 ? expand_scatter_kernel<true, true, false>
+                   : expand_scatter_kernel<true, false, false>;
+    hipLaunchKernelGGL(k, dim3((unsigned)grid), dim3(kScatterThreads), lds, s, MOE_SCATTER_ARGS);
   }
-  }
-  // One wave per received row, and enough workgroups that the label fill and
-  // the pad zeroing spread over the chip.
-  int64_t grid = (rows + kRowsPerScatterBlock - 1) / kRowsPerScatterBlock;
-  if (grid < 1024) grid = 1024;
-  if (grid > 16384) grid = 16384;
-  const size_t lds = (size_t(4) * E + 1 + (fold ? size_t(nb) * E : 0)) * 4;
-  auto scatter = !bf16 || keep ? expand_scatter_kernel<false, false>
-                 : fmt == MOE_SCALE_UE8M0 ? expand_scatter_kernel<true, true>
-                                          : expand_scatter_kernel<true, false>;
-  hipLaunchKernelGGL(scatter,
-                     dim3((unsigned)grid), dim3(kScatterThreads), lds, s,
-                     (const uint8_t*)x, x_stride, (const uint8_t*)x_scale,
-                     mx ? x_scale_stride : x_scale_stride * scale_bytes, scale_bytes, topk_ids,
-                     topk_weights,
-                     psum_recv_per_rank, num_src_ranks, rows, keep ? 2 * hidden : hidden, topk, E,
-                     capacity, align, w.grp, w.blk, G, (int)nb, w.blk_flag, fold ? 1 : 0,
-                     w.starts, w.padbase,
-                     psum, status, (uint8_t*)ex, (uint8_t*)ex_scale, m_indices, src2dst,
-                     row_weight);
+#undef MOE_SCATTER_ARGS
   if (hipGetLastError() != hipSuccess) return MOE_ERR_LAUNCH;
   return MOE_OK;
 }
