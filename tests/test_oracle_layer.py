@@ -7,7 +7,8 @@
 * SiLU*up against the float64 closed form; quantisation against its defining
   properties (the group's largest magnitude maps to 448, q*s reconstructs y
   to half an fp8 step, the fold multiplies the scale, UE8M0 scales are the
-  tight power of two).
+  tight power of two), for 1x128 rows and for 128x128 weight blocks; the
+  live-row mask on a hand case and against the layout's pad rows.
 * Gather against a hand-computed case.
 * The whole layer equals a per-token brute force with no layout (bit-exact);
   the weight fold equals post-weighting to bf16 rounding; with one expert,
@@ -145,6 +146,71 @@ def test_quant_ue8m0_properties():
     deq = quant.dequant_rows(q, b, "ue8m0")
     assert np.all(np.abs(deq - y) <= np.abs(y) * 2 ** -4 + np.repeat(s, 128, axis=1) * 2 ** -10)
     assert np.all(np.abs(fp8.decode_e4m3(q)) <= 448)
+
+
+def test_quant_blocks_properties():
+    """128x128 weight blocks: one scale per block of each expert's [N, K]
+    matrix; the block's largest magnitude maps to +-448 (fp32 scales, amax /
+    448 to one fp32 rounding in float64) or the UE8M0 byte is the tight power
+    of two (float64 ceil(log2(amax / 448)) + 127); every code reconstructs its
+    value to half an fp8 step.  Blocks are given magnitudes 2^-12 .. 2^12
+    apart, so a block mixed up with its neighbour (a transposed or shifted
+    block index) fails."""
+    rng = np.random.default_rng(6)
+    E, N, K = 2, 256, 384
+    mag = 2.0 ** rng.integers(-12, 13, (E, N // 128, K // 128))
+    w = (rng.standard_normal((E, N, K))
+         * np.repeat(np.repeat(mag, 128, axis=1), 128, axis=2)).astype(np.float32)
+    w[1, :128, 128:256] = 0.0            # an all-zero block: eps clamp
+    blocks = w.astype(np.float64).reshape(E, N // 128, 128, K // 128, 128)
+    amax = np.abs(blocks).max(axis=(2, 4))
+    for fmt in ("f32", "ue8m0"):
+        q, s = quant.quantize_blocks(w, fmt)
+        assert q.shape == (E, N, K) and s.shape == (E, N // 128, K // 128)
+        sv = quant.scale_values(s, fmt)
+        if fmt == "f32":
+            ref = np.maximum(amax, 1e-10) / 448.0
+            assert np.all(np.abs(sv - ref) <= ref * 2.0 ** -23)
+            qb = q.reshape(E, N // 128, 128, K // 128, 128)
+            for e in range(E):
+                for i in range(N // 128):
+                    for j in range(K // 128):
+                        if amax[e, i, j] == 0:
+                            assert not qb[e, i, :, j, :].any()
+                            continue
+                        a = np.abs(blocks[e, i, :, j, :])
+                        r, c = np.unravel_index(a.argmax(), a.shape)
+                        assert qb[e, i, r, j, c] & 0x7F == 0x7E    # +-448
+        else:
+            live = amax > 0
+            need = np.log2(amax[live] / 448.0)
+            assert np.array_equal(s[live].astype(np.int64), np.ceil(need).astype(np.int64) + 127)
+        deq = np.stack([quant.dequant_block(q[e], s[e], fmt) for e in range(E)])
+        scale = np.repeat(np.repeat(sv, 128, axis=1), 128, axis=2)
+        scaled = np.abs(w.astype(np.float64)) / scale
+        step = np.where(scaled >= 2 ** -6,
+                        2.0 ** (np.floor(np.log2(np.maximum(scaled, 1e-300))) - 3), 2.0 ** -9)
+        assert np.all(np.abs(deq - w) <= 0.5 * step * scale * (1 + 1e-6))
+
+
+def test_live_rows_hand_case():
+    """Row m of expert e's block is live below psum[e]; the block's alignment
+    pads and rows labelled -1 are not.  Counts 3, 0, 5 with alignment 4:
+    psum = [3, 4 + 0, 4 + 5] = [3, 4, 9], blocks [0, 4), [4, 4), [4, 12)."""
+    psum = np.array([3, 4, 9], np.int32)
+    mi = np.array([0, 0, 0, 0, 2, 2, 2, 2, 2, 2, 2, 2, -1, -1], np.int32)
+    live = layer.live_rows(mi, psum, 4, 14)
+    assert live.tolist() == [1, 1, 1, 0, 1, 1, 1, 1, 1, 0, 0, 0, 0, 0]
+    # a total cut short of the padded block end (capacity clamp)
+    assert layer.live_rows(mi, psum, 4, 6).tolist() == [1, 1, 1, 0, 1, 1]
+    # agrees with the layout's own pad rows on a random routing
+    rng = np.random.default_rng(7)
+    ids = rng.integers(-1, 6, (300, 3)).astype(np.int32)
+    lay = layout.expand_layout(ids, 300, 6, 16, layout.capacity(300, 3, 6, 16))
+    n = lay["total"]
+    live = layer.live_rows(lay["m_indices"], lay["psum"], 16, n)
+    src = lay["src2dst"]
+    assert live.sum() == (src >= 0).sum() and np.all(live[src[src >= 0]])
 
 
 def test_act_quant_fold_and_pad_rows():
