@@ -707,6 +707,87 @@ __device__ __forceinline__ void kloop_role(int role, uint32_t lds0, v4f (&acc)[F
   }
 }
 
+// Row groups: expert e's block [start_e, end_e) (clamped to the valid rows)
+// is cut into ceil(len / GM) groups.  Wave 0 writes gp (prefix of groups per
+// expert, gp[E] = all) and pe (end of each expert's live rows) into LDS.
+// kMasked: `psum` is masked_m, `align` is max_m.
+template <bool kMasked>
+__device__ __forceinline__ void build_groups(const int32_t* __restrict__ psum, int64_t nrows,
+                                             int E, int align, int* gp, int* pe, int lane) {
+  int run = 0;
+  for (int e0 = 0; e0 < E; e0 += 64) {
+    const int e = e0 + lane;
+    int ng = 0;
+    if (e < E) {
+      if (kMasked) {  // slab: rows [e * max_m, + masked_m[e]), no padding
+        const int64_t st = (int64_t)e * align;
+        const int64_t en = st + max(0, min(psum[e], align));
+        ng = (int)((en - st + GM - 1) / GM);
+        pe[e] = (int)en;
+      } else {
+        const int p_e = psum[e];
+        const int64_t st = e ? align_up_i(psum[e - 1], align) : 0;
+        const int64_t en = min((int64_t)align_up_i(p_e, align), nrows);
+        ng = en > st ? (int)((en - st + GM - 1) / GM) : 0;
+        pe[e] = p_e;
+      }
+    }
+    const int incl = wave_incl_scan_i(ng);
+    if (e < E) gp[e] = run + incl - ng;
+    run += __shfl(incl, 63, 64);
+  }
+  if (lane == 0) gp[E] = run;
+}
+
+// Work item `item` -> its Item (false: only alignment padding, nothing to
+// compute); nt and m0 are its N tile and first row.  Expert e's items are
+// [NT * gp[e], NT * gp[e + 1]), N-tile-major with its row groups innermost:
+// the groups of one (expert, N tile) share a weight stream and run side by
+// side on one XCD, so its L2 serves the weights to all but one of them.
+template <int kFmt, bool kMasked>
+__device__ __forceinline__ bool decode_item(
+    int64_t item, const int* gp, const int* pe, int E, int NT, int KB, int K, int N,
+    int64_t nrows, int align, int64_t capacity, const uint8_t* a, const uint8_t* a_scale,
+    const uint8_t* w, const uint8_t* w_scale, int sbytes, uint32_t wsc_lds, Item& it, int& nt,
+    int64_t& m0) {
+  const int q = (int)(item / NT);
+  int lo = 0, hi = E - 1;  // last e with gp[e] <= q
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (gp[mid] <= q) lo = mid;
+    else hi = mid - 1;
+  }
+  const int e = lo;
+  const int ge = gp[e + 1] - gp[e];  // row groups of expert e (>= 1 here)
+  const int64_t local = item - (int64_t)NT * gp[e];
+  nt = (int)(local / ge);
+  const int gi = gp[e] + (int)(local % ge);
+  const int64_t st = kMasked ? (int64_t)e * align : (e ? align_up_i(pe[e - 1], align) : 0);
+  m0 = st + (int64_t)(gi - gp[e]) * GM;
+  const int64_t live = min((int64_t)GM, min((int64_t)pe[e], nrows) - m0);
+  if (live <= 0) return false;
+  it.live = (int)live;
+  it.K = K;
+  it.KB = KB;
+  // Staggered K start for the first round (see the header).
+  it.k0 = item < (int64_t)gridDim.x ? (int)(((int64_t)nt * KB) / NT) : 0;
+  it.sbytes = sbytes;
+  it.blocks = ((int)live + 7) >> 3;
+  it.na = (it.blocks + kLoadWaves - 1) / kLoadWaves;  // 1..8
+  it.a_slot_bytes = it.na * 4096;
+  it.na_slots = act_slots(it.na);
+  it.a = a + m0 * K;
+  it.b = w + ((int64_t)e * N + (int64_t)nt * BN) * K;
+  it.ws = kFmt == kMX ? w_scale + ((int64_t)e * N + (int64_t)nt * BN) * (K / 32) : nullptr;
+  it.wsc_lds = wsc_lds;
+  it.as = a_scale + m0 * sbytes;
+  it.as_kstride = capacity * sbytes;
+  const int64_t b0 = ((int64_t)e * NT + nt) * KB * sbytes;  // byte of block 0's scale
+  it.bs = w_scale + (b0 & ~(int64_t)3);
+  it.bs_skew = (int)(b0 & 3);
+  return true;
+}
+
 // kMasked: `psum` is masked_m, `align` is max_m, `status` is unused and the
 // activation rows are the E * max_m slab rows (capacity).
 template <int kFmt, bool kMasked>
@@ -729,80 +810,19 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(
   const int sbytes = kFmt == kU8 ? 1 : (kFmt == kF32 || kFmt == kMX ? 4 : 0);
   const int KB = K / BK, NT = N / BN;
 
-  // Row groups: expert e's block [start_e, end_e) (clamped to the valid rows)
-  // is cut into ceil(len / GM) groups.
-  if (wid == 0) {
-    int run = 0;
-    for (int e0 = 0; e0 < E; e0 += 64) {
-      const int e = e0 + lane;
-      int ng = 0;
-      if (e < E) {
-        if (kMasked) {  // slab: rows [e * max_m, + masked_m[e]), no padding
-          const int64_t st = (int64_t)e * align;
-          const int64_t en = st + max(0, min(psum[e], align));
-          ng = (int)((en - st + GM - 1) / GM);
-          pe[e] = (int)en;
-        } else {
-          const int p_e = psum[e];
-          const int64_t st = e ? align_up_i(psum[e - 1], align) : 0;
-          const int64_t en = min((int64_t)align_up_i(p_e, align), nrows);
-          ng = en > st ? (int)((en - st + GM - 1) / GM) : 0;
-          pe[e] = p_e;
-        }
-      }
-      const int incl = wave_incl_scan_i(ng);
-      if (e < E) gp[e] = run + incl - ng;
-      run += __shfl(incl, 63, 64);
-    }
-    if (lane == 0) gp[E] = run;
-  }
+  if (wid == 0) build_groups<kMasked>(psum, nrows, E, align, gp, pe, lane);
   __syncthreads();
   const int64_t nitems = (int64_t)gp[E] * NT;
   const int per_xcd = gridDim.x / kXcds;
   const int64_t slot = (int64_t)(blockIdx.x % kXcds) * per_xcd + blockIdx.x / kXcds;
 
   for (int64_t item = slot; item < nitems; item += gridDim.x) {
-    // Expert e's items are [NT * gp[e], NT * gp[e + 1]), N-tile-major with
-    // its row groups innermost: the groups of one (expert, N tile) share a
-    // weight stream and run side by side on one XCD, so its L2 serves the
-    // weights to all but one of them.
-    const int q = (int)(item / NT);
-    int lo = 0, hi = E - 1;  // last e with gp[e] <= q
-    while (lo < hi) {
-      const int mid = (lo + hi + 1) >> 1;
-      if (gp[mid] <= q) lo = mid;
-      else hi = mid - 1;
-    }
-    const int e = lo;
-    const int ge = gp[e + 1] - gp[e];  // row groups of expert e (>= 1 here)
-    const int64_t local = item - (int64_t)NT * gp[e];
-    const int nt = (int)(local / ge), gi = gp[e] + (int)(local % ge);
-    const int64_t st = kMasked ? (int64_t)e * align : (e ? align_up_i(pe[e - 1], align) : 0);
-    const int64_t m0 = st + (int64_t)(gi - gp[e]) * GM;
-    const int64_t live = min((int64_t)GM, min((int64_t)pe[e], nrows) - m0);
-    if (live <= 0) continue;  // only alignment padding: nothing to compute
     Item it;
-    it.live = (int)live;
-    it.K = K;
-    it.KB = KB;
-    // Staggered K start for the first round (see the header).
-    it.k0 = item < (int64_t)gridDim.x ? (int)(((int64_t)nt * KB) / NT) : 0;
-    it.sbytes = sbytes;
-    it.blocks = ((int)live + 7) >> 3;
-    it.na = (it.blocks + kLoadWaves - 1) / kLoadWaves;  // 1..8
-    it.a_slot_bytes = it.na * 4096;
-    it.na_slots = act_slots(it.na);
-    it.a = a + m0 * K;
-    it.b = w + ((int64_t)e * N + (int64_t)nt * BN) * K;
-    it.ws = kFmt == kMX ? w_scale + ((int64_t)e * N + (int64_t)nt * BN) * (K / 32) : nullptr;
-    it.wsc_lds = lds_addr(wsc);
-    it.as = a_scale + m0 * sbytes;
-    it.as_kstride = capacity * sbytes;
-    {
-      const int64_t b0 = ((int64_t)e * NT + nt) * KB * sbytes;  // byte of block 0's scale
-      it.bs = w_scale + (b0 & ~(int64_t)3);
-      it.bs_skew = (int)(b0 & 3);
-    }
+    int nt;
+    int64_t m0;
+    if (!decode_item<kFmt, kMasked>(item, gp, pe, E, NT, KB, K, N, nrows, align, capacity, a,
+                                     a_scale, w, w_scale, sbytes, lds_addr(wsc), it, nt, m0))
+      continue;  // only alignment padding: nothing to compute
     // Live 16-row MFMA tiles of this wave, and the loads it issues per stage.
     const int nfm = (int)max(0, min(FM, (it.live - wm * 16 + ROW_TILE_STRIDE - 1) /
                                             ROW_TILE_STRIDE));
