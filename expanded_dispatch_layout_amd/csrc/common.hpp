@@ -40,14 +40,18 @@ __device__ __forceinline__ int wave_or_i(int v) {
   for (int o = 32; o > 0; o >>= 1) v |= __shfl_xor(v, o, kWave);
   return v;
 }
-// Inclusive prefix sum over lanes.
+// Inclusive prefix sum over lanes, with DPP moves (VALU, a few cycles each,
+// where a shuffle is an LDS-crossbar round trip): a Hillis-Steele scan within
+// each row of 16 lanes (row_shr 1, 2, 4, 8; lanes whose source falls before
+// the row keep 0), then lane 15's total added to rows 1 and 3 (row_bcast:15)
+// and lane 31's to rows 2 and 3 (row_bcast:31).  Every lane must be active.
 __device__ __forceinline__ int wave_incl_scan_i(int v) {
-  const int lane = threadIdx.x & (kWave - 1);
-#pragma unroll
-  for (int o = 1; o < kWave; o <<= 1) {
-    int t = __shfl_up(v, o, kWave);
-    if (lane >= o) v += t;
-  }
+  v += __builtin_amdgcn_update_dpp(0, v, 0x111, 0xf, 0xf, false);  // row_shr:1
+  v += __builtin_amdgcn_update_dpp(0, v, 0x112, 0xf, 0xf, false);  // row_shr:2
+  v += __builtin_amdgcn_update_dpp(0, v, 0x114, 0xf, 0xf, false);  // row_shr:4
+  v += __builtin_amdgcn_update_dpp(0, v, 0x118, 0xf, 0xf, false);  // row_shr:8
+  v += __builtin_amdgcn_update_dpp(0, v, 0x142, 0xa, 0xf, false);  // row_bcast:15
+  v += __builtin_amdgcn_update_dpp(0, v, 0x143, 0xc, 0xf, false);  // row_bcast:31
   return v;
 }
 

@@ -306,17 +306,26 @@ struct RowIds {
     }
     if (lane < topk) myid = ids[r * topk + lane];
   }
+  // Rows loaded against the buffer's size, then cut at the valid-row bound.
+  __device__ __forceinline__ void clip(int64_t r, int64_t nv) {
+    if (r < nv) return;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) prev[i] = -1;
+    myid = -1;
+  }
 };
 
 // The loads of a row with a local slot that do not depend on the
 // destinations: its first 8 KB, its first 64 scales, each local slot's
-// weight and its group's offset within its block.
+// weight, its group's offset within its block and (block table in global
+// memory) the block's offset: issued together, before the next row's
+// prefetch, so that computing the destinations waits for nothing later.
 struct RowData {
   u32x4 v[8];
-  float sf;
-  uint8_t sb;
+  uint32_t sc;  // the scale: fp32 bits, a 4-byte MXFP8 word or a UE8M0 byte
   float wt;
   int grp;
+  int blk;
 
   // kQ: the row is bf16 (2 bytes per element) and has no scales.  mine: this
   // lane's slot is local (lane k < topk holds slot k).
@@ -325,7 +334,8 @@ struct RowData {
                                        const uint8_t* __restrict__ x_scale,
                                        int64_t x_scale_stride_bytes, int scale_bytes,
                                        const float* __restrict__ topk_w,
-                                       const int32_t* __restrict__ grp_off, bool weights,
+                                       const int32_t* __restrict__ grp_off,
+                                       const int32_t* __restrict__ blk_off, int G, bool weights,
                                        int64_t r, int hidden, int topk, int E, int lane,
                                        bool mine, int myid) {
     const int nch = kQ ? hidden / 8 : hidden / 16, nsc = hidden / kGroup;
@@ -336,17 +346,18 @@ struct RowData {
       const int c = u * 64 + lane;
       if (c < nch) v[u] = src[c];
     }
-    sf = 0.f;
-    sb = 0;
-    if (!kQ && scale_bytes && lane < nsc) {
-      if (scale_bytes == 4) sf = reinterpret_cast<const float*>(srow)[lane];
-      else sb = srow[lane];
-    }
+    // (one register for either width: two registers, each written by a load
+    // on one branch only, make the compiler wait for every load in flight)
+    sc = 0u;
+    if (!kQ && scale_bytes && lane < nsc)
+      sc = scale_bytes == 4 ? reinterpret_cast<const uint32_t*>(srow)[lane] : srow[lane];
     wt = 0.f;
     grp = 0;
+    blk = 0;
     if (mine) {
       if (weights) wt = topk_w[r * topk + lane];
       if (grp_off) grp = grp_off[(r / kGroupRows) * E + myid];
+      if (blk_off) blk = blk_off[(r / kGroupRows / G) * E + myid];
     }
   }
 };
@@ -397,46 +408,117 @@ __device__ __forceinline__ void quant_pass(const u32x4 (&v)[8], int c0, int nch,
 }
 
 // Count of the valid slots with local ids, per expert, over the whole
-// receive buffer (into tot) and over the slots before `npre` (into pre):
-// every workgroup of the fused launch runs this itself.  ids are read as
-// 16-byte vectors when aligned (four slots each), eight in flight per
-// thread; only local ids touch LDS (one atomic add each).
+// receive buffer (into tot) and over the slots before `npre` (into pre), for
+// E <= 8: every workgroup of the fused launch runs this itself (at most
+// kFusedSlots slots, so 32-bit slot indices); tot and pre are cleared here.
+// The loads cover all `nall` slots of the buffer, so that they need not wait
+// for the valid-row bound; slots at or past `nslot` are not counted.  ids are
+// read as 16-byte vectors when aligned (four slots each), eight in flight
+// per thread.
+// Each thread keeps its counts in 7-bit fields of a 64-bit word, expert e
+// in field e and every id outside [0, 8) in a ninth field that is never read,
+// so a slot costs a min, a multiply, a shift and an add with no compare; ids
+// >= E are caught by a running max.  npre is a multiple of 4 or equal to
+// nslot, so a vector of four valid slots lies wholly before or after it.
+// The words are widened to 16-bit fields and summed over the wave by a
+// transpose-reduce (DPP moves within rows of 16 lanes, two shuffles across
+// rows), and eight lanes per wave add the sums to LDS.
+__device__ __forceinline__ uint64_t slot_inc7(int id) {
+  return 1ull << (min((unsigned)id, 8u) * 7u);
+}
+
+// a + the value of lane (lane ^ m) within rows of 16 lanes, m = 1, 2, 7, 8
+template <int kCtrl>
+__device__ __forceinline__ uint32_t dpp_add(uint32_t keep, uint32_t send) {
+  return keep + (uint32_t)__builtin_amdgcn_update_dpp(0, (int)send, kCtrl, 0xf, 0xf, false);
+}
+
 template <int NTH>
-__device__ __forceinline__ void count_all(const int32_t* __restrict__ ids, int64_t nslot,
-                                          int64_t npre, int E, bool vec, int32_t* tot,
+__device__ __forceinline__ void count_all(const int32_t* __restrict__ ids, int nall, int nslot,
+                                          int npre, int E, bool vec, int32_t* tot,
                                           int32_t* pre, int& bad) {
-  const int t = threadIdx.x;
-  auto one = [&](int id, int64_t s) __attribute__((always_inline)) {
-    if (id >= E) bad = 1;
-    else if (id >= 0) {
-      atomicAdd(&tot[id], 1);
-      if (s < npre) atomicAdd(&pre[id], 1);
+  static_assert(kFusedSlots / NTH + 1 <= 127, "7-bit per-thread counters");
+  const int t = threadIdx.x, lane = t & 63;
+  uint64_t ct = 0ull, cp = 0ull;
+  int mx = -1;
+  auto one = [&](int id, int s) __attribute__((always_inline)) {  // any slot
+    if (s < nslot) {
+      const uint64_t inc = slot_inc7(id);
+      ct += inc;
+      if (s < npre) cp += inc;
+      mx = max(mx, id);
     }
   };
-  int64_t done = 0;
+  int done = 0;
   if (vec) {
-    const int64_t n4 = nslot >> 2;
+    const int n4 = nall >> 2;
     const int4* ids4 = reinterpret_cast<const int4*>(ids);
     constexpr int U = 8;
-    for (int64_t i0 = 0; i0 < n4; i0 += (int64_t)U * NTH) {
+    for (int i0 = 0; i0 < n4; i0 += U * NTH) {
       int4 v[U];
 #pragma unroll
       for (int u = 0; u < U; ++u) {
-        const int64_t i = i0 + u * NTH + t;
+        const int i = i0 + u * NTH + t;
         v[u] = i < n4 ? ids4[i] : make_int4(-1, -1, -1, -1);
       }
 #pragma unroll
       for (int u = 0; u < U; ++u) {
-        const int64_t s = (i0 + u * NTH + t) * 4;
-        one(v[u].x, s);
-        one(v[u].y, s + 1);
-        one(v[u].z, s + 2);
-        one(v[u].w, s + 3);
+        const int s = (i0 + u * NTH + t) * 4;
+        if (s + 4 <= nslot) {  // four valid slots
+          const uint64_t q = slot_inc7(v[u].x) + slot_inc7(v[u].y) + slot_inc7(v[u].z) +
+                             slot_inc7(v[u].w);
+          ct += q;
+          cp += s < npre ? q : 0ull;
+          mx = max(mx, max(max(v[u].x, v[u].y), max(v[u].z, v[u].w)));
+        } else if (s < nslot) {
+          one(v[u].x, s);
+          one(v[u].y, s + 1);
+          one(v[u].z, s + 2);
+          one(v[u].w, s + 3);
+        }
       }
     }
     done = n4 * 4;
   }
-  for (int64_t s = done + t; s < nslot; s += NTH) one(ids[s], s);
+  for (int s = done + t; s < nslot; s += NTH) one(ids[s], s);
+  bad |= (int)(mx >= E);
+  // 16-bit fields: word k holds experts 2 (k & 3) and 2 (k & 3) + 1 of tot
+  // (k < 4) or pre (k >= 4).
+  uint32_t w[8];
+#pragma unroll
+  for (int k = 0; k < 8; ++k) {
+    const uint64_t x = k < 4 ? ct : cp;
+    const int e = 2 * (k & 3);
+    w[k] = (uint32_t)((x >> (7 * e)) & 127u) | ((uint32_t)((x >> (7 * e + 7)) & 127u) << 16);
+  }
+  // Transpose-reduce: each step pairs lanes that differ in one bit of
+  // (lane & 7), each lane keeping half of its words (chosen by that bit)
+  // plus its partner's copy of them; lane l ends with word l & 7 summed over
+  // its 8 lanes, then over the wave.  (row_half_mirror pairs l with l ^ 7,
+  // which differ in bit 2, while every lane still holds all eight words.)
+  const bool b2 = lane & 4, b1 = lane & 2, b0 = lane & 1;
+  uint32_t h[4], g[2];
+#pragma unroll
+  for (int j = 0; j < 4; ++j)
+    h[j] = dpp_add<0x141>(b2 ? w[4 + j] : w[j], b2 ? w[j] : w[4 + j]);  // row_half_mirror
+#pragma unroll
+  for (int j = 0; j < 2; ++j)
+    g[j] = dpp_add<0x4e>(b1 ? h[2 + j] : h[j], b1 ? h[j] : h[2 + j]);  // quad_perm 2,3,0,1
+  uint32_t sum = dpp_add<0xb1>(b0 ? g[1] : g[0], b0 ? g[0] : g[1]);  // quad_perm 1,0,3,2
+  sum = dpp_add<0x128>(sum, sum);                                     // row_ror:8 (lane ^ 8)
+  sum += (uint32_t)__shfl_xor((int)sum, 16, 64);
+  sum += (uint32_t)__shfl_xor((int)sum, 32, 64);
+  for (int e = t; e < E; e += NTH) {
+    tot[e] = 0;
+    pre[e] = 0;
+  }
+  __syncthreads();  // (no barrier before the loads above)
+  if (lane < 8) {
+    int32_t* dst = lane < 4 ? tot : pre;
+    const int e = 2 * (lane & 3);
+    if (e < E && (sum & 0xffffu)) atomicAdd(&dst[e], (int)(sum & 0xffffu));
+    if (e + 1 < E && (sum >> 16)) atomicAdd(&dst[e + 1], (int)(sum >> 16));
+  }
 }
 
 // kQ: bf16 input rows quantised here (x_scale unused), with UE8M0 scales
@@ -478,34 +560,65 @@ __global__ __launch_bounds__(kFused ? kFusedThreads : kScatterThreads) void expa
   const int64_t r_step = kFused ? NT / 64 : gwaves;
   const bool weights = row_weight != nullptr;
   const int32_t* grp_tab = kFused ? nullptr : grp_off;
+  const int32_t* blk_tab = kFused || fold ? nullptr : blk_g;  // else the LDS copy
 
   // The first row's ids (and, fold, the first 256 entries of the count
   // kernel's block table, which is all of it at the DeepSeek-V3 share) are
   // requested before anything waits.
-  const int nbe = fold ? nblk * E : 0;
+  // (Never in the fused kernel: a register left waiting for such a load
+  // makes the compiler drain every load in flight before it is reused.)
+  const bool fold_c = !kFused && fold;
+  const int nbe = fold_c ? nblk * E : 0;
   const int blk0 = t < nbe ? blk_g[t] : 0;
-  const int flg0 = (fold && t < nblk) ? blk_flag[t] : 0;
+  const int flg0 = (fold_c && t < nblk) ? blk_flag[t] : 0;
+  // (fused: loaded against the buffer's size, so that no load waits for the
+  // valid-row bound, and cut at the bound once it is known)
   RowIds ia;
-  if (r_first < r_end) ia.load(ids, r_first, nv, topk, lane);
+  if (r_first < r_end) ia.load(ids, r_first, kFused ? rows : nv, topk, lane);
   if (t < nbe) l_blk[t] = blk0;
-  const int32_t* blk_off;  // per-expert offset of a row's group: [nblk][E] or [E]
+  // The first row's data: fused, requested as soon as the count is in (its
+  // ids arrived before the count's), so that it is in flight during the
+  // scan; otherwise once the tables are read.
+  RowData da;
+  bool mine_a = false;
+  uint64_t live_a = 0ull;
+  auto start_a = [&]() __attribute__((always_inline)) {
+    if (kFused) ia.clip(r_first, nv);
+    mine_a = r_first < r_end && ia.myid >= 0 && ia.myid < E;
+    live_a = __ballot(mine_a);
+    if (r_first < r_end && live_a)
+      da.load<kQ>(x, x_stride, x_scale, x_scale_stride_bytes, scale_bytes, topk_w, grp_tab,
+                  blk_tab, G, weights, r_first, hidden, topk, E, lane, mine_a, ia.myid);
+  };
   if (kFused || fold) {
     if (t == 0) l_flag = 0;
     int fl = 0;
     if constexpr (kFused) {
-      for (int e = t; e < E; e += NT) {
-        l_psum[e] = 0;  // totals
-        l_blk[e] = 0;   // counts before this group
-      }
-      __syncthreads();
-      count_all<NT>(ids, nv * topk, min(g0, nv) * topk, E, ids_vec != 0, l_psum, l_blk, fl);
+      // l_psum: totals; l_blk: counts before this group
+      const int nall = (int)rows * topk, nsl = (int)nv * topk, npre = (int)min(g0, nv) * topk;
+      count_all<NT>(ids, nall, nsl, npre, E, ids_vec != 0, l_psum, l_blk, fl);
       fl = fl ? MOE_FLAG_EXPERT_ID_RANGE : 0;
+      start_a();
     } else {
       // The scan over the (few) block totals, done by every workgroup: block
-      // offsets per expert, expert totals, aligned starts, pad prefix.
-      for (int i = t + NT; i < nbe; i += NT) l_blk[i] = blk_g[i];
+      // offsets per expert, expert totals, aligned starts, pad prefix.  The
+      // rest of the table and of the flags: every load issued before any is
+      // used (one round trip, not one per pass).
+      constexpr int kPer = kFoldScanInts / NT;
+      int rest[kPer - 1], frest[kPer - 1];
+#pragma unroll
+      for (int j = 1; j < kPer; ++j) {
+        const int i = t + j * NT;
+        rest[j - 1] = i < nbe ? blk_g[i] : 0;
+        frest[j - 1] = i < nblk ? blk_flag[i] : 0;
+      }
       fl = flg0;
-      for (int b = t + NT; b < nblk; b += NT) fl |= blk_flag[b];
+#pragma unroll
+      for (int j = 1; j < kPer; ++j) {
+        const int i = t + j * NT;
+        if (i < nbe) l_blk[i] = rest[j - 1];
+        fl |= frest[j - 1];
+      }
     }
     __syncthreads();
     if (fl) atomicOr(&l_flag, fl);
@@ -573,7 +686,6 @@ __global__ __launch_bounds__(kFused ? kFusedThreads : kScatterThreads) void expa
         status[1] = l_flag | (total > capacity ? MOE_FLAG_CAPACITY_OVERFLOW : 0);
       }
     }
-    blk_off = l_blk;
   } else {
     for (int i = t; i < E; i += NT) {
       l_starts[i] = starts_g[i];
@@ -582,7 +694,6 @@ __global__ __launch_bounds__(kFused ? kFusedThreads : kScatterThreads) void expa
     for (int i = t; i <= E; i += NT) l_padbase[i] = padbase_g[i];
     if (t == 0) l_total = status[0];
     __syncthreads();
-    blk_off = blk_g;
   }
   const int total = l_total;
   const int64_t nrows_ex = min((int64_t)total, capacity);
@@ -592,12 +703,7 @@ __global__ __launch_bounds__(kFused ? kFusedThreads : kScatterThreads) void expa
 
   // ---- the wave's rows, software-pipelined: while row r is stored, the
   // data of the next row and the ids of the row after are in flight ----
-  RowData da;
-  bool mine_a = ia.myid >= 0 && ia.myid < E;
-  uint64_t live_a = __ballot(mine_a);
-  if (r_first < r_end && live_a)
-    da.load<kQ>(x, x_stride, x_scale, x_scale_stride_bytes, scale_bytes, topk_w, grp_tab, weights,
-                r_first, hidden, topk, E, lane, mine_a, ia.myid);
+  if constexpr (!kFused) start_a();
   RowIds ib;  // (fused: each wave has one row, nothing to prefetch)
   if (!kFused && r_first + r_step < r_end) ib.load(ids, r_first + r_step, nv, topk, lane);
   for (int64_t r = r_first; r < r_end; r += r_step) {
@@ -616,7 +722,7 @@ __global__ __launch_bounds__(kFused ? kFusedThreads : kScatterThreads) void expa
       if (rn + r_step < r_end) ic.load(ids, rn + r_step, nv, topk, lane);
       if (live_b)
         db.load<kQ>(x, x_stride, x_scale, x_scale_stride_bytes, scale_bytes, topk_w, grp_tab,
-                    weights, rn, hidden, topk, E, lane, mine_b, ib.myid);
+                    blk_tab, G, weights, rn, hidden, topk, E, lane, mine_b, ib.myid);
     }
 
     if (live_a == 0) {
@@ -636,8 +742,10 @@ __global__ __launch_bounds__(kFused ? kFusedThreads : kScatterThreads) void expa
       }
       int d = -1;
       if (mine_a) {
-        const int64_t off = kFused ? (int64_t)blk_off[ia.myid]
-                                   : (int64_t)blk_off[(g / G) * E + ia.myid] + da.grp;
+        // (l_blk is LDS: the fused counts before this group, or the folded
+        // block table; otherwise the block offset came with the row's data)
+        const int64_t off = kFused ? (int64_t)l_blk[ia.myid]
+                            : (int64_t)(fold ? l_blk[(g / G) * E + ia.myid] : da.blk) + da.grp;
         const int64_t dd = (int64_t)l_starts[ia.myid] + off + rank;
         if (dd < capacity) {
           d = (int)dd;
@@ -698,16 +806,15 @@ __global__ __launch_bounds__(kFused ? kFusedThreads : kScatterThreads) void expa
           for (int c0 = 0; c0 < nsc; c0 += 64) {
             const int c = c0 + lane;
             if (c0 > 0 && c < nsc) {
-              if (scale_bytes == 4) da.sf = reinterpret_cast<const float*>(srow)[c];
-              else da.sb = srow[c];
+              da.sc = scale_bytes == 4 ? reinterpret_cast<const uint32_t*>(srow)[c] : srow[c];
             }
             // ex_scale is K-block-major: scale (row dk, block c) at c * capacity + dk.
             for (uint64_t mm = mask; mm; mm &= mm - 1) {
               const int dk = __shfl(d, __builtin_ctzll(mm), 64);
               if (c < nsc) {
                 const int64_t at = (int64_t)c * capacity + dk;
-                if (scale_bytes == 4) reinterpret_cast<float*>(ex_scale)[at] = da.sf;
-                else ex_scale[at] = da.sb;
+                if (scale_bytes == 4) reinterpret_cast<uint32_t*>(ex_scale)[at] = da.sc;
+                else ex_scale[at] = (uint8_t)da.sc;
               }
             }
           }
@@ -819,7 +926,8 @@ moe_status expand_layout(bool bf16, const void* x, int64_t x_stride, const void*
   // threads) counts the whole buffer's valid slots itself (at most
   // kFusedSlots ids, one round trip from L2) and owns one 16-row group, a
   // wave per row: one launch for the whole layout.
-  const bool fused = rows * topk <= kFusedSlots && !(bf16 && !keep);  // (quantising: registers)
+  // (not when quantising, for registers; E <= 8: per-thread counters)
+  const bool fused = rows * topk <= kFusedSlots && !(bf16 && !keep) && E <= 8;
   // Otherwise: count kernel; a small block table is scanned by every scatter
   // workgroup itself (no scan kernel), a large one by the scan kernel once.
   const bool fold = !fused && nb * E <= kFoldScanInts;
@@ -854,11 +962,9 @@ moe_status expand_layout(bool bf16, const void* x, int64_t x_stride, const void*
       topk_weights, psum_recv_per_rank, num_src_ranks, rows, hdim, topk, E, capacity, align,   \
       w.grp, w.blk, G, (int)nb, w.blk_flag, fold ? 1 : 0, w.starts, w.padbase, psum, status,   \
       (uint8_t*)ex, (uint8_t*)ex_scale, m_indices, src2dst, row_weight, ids_vec
-  if (fused) {
-    auto k = !q ? expand_scatter_kernel<false, false, true>
-             : qu8 ? expand_scatter_kernel<true, true, true>
-                   : expand_scatter_kernel<true, false, true>;
-    hipLaunchKernelGGL(k, dim3((unsigned)grid), dim3(kFusedThreads), lds, s, MOE_SCATTER_ARGS);
+  if (fused) {  // (never quantising)
+    hipLaunchKernelGGL((expand_scatter_kernel<false, false, true>), dim3((unsigned)grid),
+                       dim3(kFusedThreads), lds, s, MOE_SCATTER_ARGS);
   } else {
     auto k = !q ? expand_scatter_kernel<false, false, false>
              : qu8 ? expand_scatter_kernel<true, true, false>
