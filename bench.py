@@ -392,23 +392,30 @@ def main():
     total_ms = t_start.elapsed_time(t_end)
     ms_step = total_ms / args.steps
 
-    # The dominant kernel's launch durations: K more whole steps, with events
-    # around its two launches (gate_up, down) on the stream they run on.
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    # Kernel durations: K more whole steps with an event between every two
+    # kernels.  Each window holds one kernel plus the cost of the marker
+    # before it (the command processor handles the event packet before it
+    # dispatches the kernel), so the windows of a step add up to more than
+    # the un-evented step time of the timed region.  That excess, shared out
+    # over the step's NS windows, is the marker cost delta; each kernel's
+    # duration is its mean window minus delta.  (These agree with the
+    # kernel-trace durations of the same command to a few percent; the raw
+    # windows and delta are reported too.)
+    sev = [[torch.cuda.Event(enable_timing=True) for _ in range(NS + 1)]
+           for _ in range(args.steps)]
     for s in range(args.steps):
+        sev[s][0].record()
         for i in range(NS):
-            if i == i_g1:
-                ev[s][0].record()
-            elif i == i_g2:
-                ev[s][2].record()
             stage(i)
-            if i == i_g1:
-                ev[s][1].record()
-            elif i == i_g2:
-                ev[s][3].record()
+            sev[s][i + 1].record()
     torch.cuda.synchronize()
-    gemm1_us = float(np.mean([e[0].elapsed_time(e[1]) for e in ev])) * 1e3
-    gemm2_us = float(np.mean([e[2].elapsed_time(e[3]) for e in ev])) * 1e3
+    windows_us = [float(np.mean([sev[s][i].elapsed_time(sev[s][i + 1])
+                                 for s in range(args.steps)])) * 1e3 for i in range(NS)]
+    delta_us = max(0.0, (sum(windows_us) - ms_step * 1e3) / NS)
+    kernel_us = [w - delta_us for w in windows_us]
+    stages_us = {n: kernel_us[i] for i, n in enumerate(names)}
+    gemm1_us, gemm2_us = kernel_us[i_g1], kernel_us[i_g2]
+    del sev
 
     # Weight rotation: K more steps cycling through three weight sets (the
     # first plus two more drawn the same way), so that no step finds the
@@ -454,17 +461,6 @@ def main():
                     "ms_per_step": r0.elapsed_time(r1) / args.steps}
         del sets
 
-    # Per-stage breakdown (after the timed region; events between stages).
-    sev = [[torch.cuda.Event(enable_timing=True) for _ in range(NS + 1)] for _ in range(10)]
-    for s in range(10):
-        sev[s][0].record()
-        for i in range(NS):
-            stage(i)
-            sev[s][i + 1].record()
-    torch.cuda.synchronize()
-    stages_us = {n: float(np.median([sev[s][i].elapsed_time(sev[s][i + 1]) for s in range(10)]))
-                 * 1e3 for i, n in enumerate(names)}
-
     status = mod.status.cpu().tolist()
     counts = np.bincount(inp["data"]["ids"][:inp["num_valid"]].reshape(-1)
                          .clip(-1, wl.experts - 1) + 1, minlength=wl.experts + 1)[1:]
@@ -494,18 +490,19 @@ def main():
                       f"{'masked' if masked else 'contiguous'}> "
                       "(mean over its gate_up and down launches)")
     roof["launch_us"] = {"gate_up": gemm1_us, "down": gemm2_us, "mean": (gemm1_us + gemm2_us) / 2}
-    roof["durations"] = ("HIP events recorded around each of the kernel's two launches per "
-                         "step on the launch stream, mean over K steps run right after the "
-                         "timed region (a window includes ~1-2 us of dispatch latency, so "
-                         "frac errs low against the kernel-trace durations)")
+    roof["durations"] = ("HIP events between every two kernels of K more steps on the launch "
+                         "stream; each kernel's mean window less the per-marker cost delta = "
+                         "(sum of a step's windows - the timed region's step time) / kernels "
+                         "per step")
+    roof["event_windows_us"] = {n: windows_us[i] for i, n in enumerate(names)}
+    roof["marker_delta_us"] = delta_us
     roof["algorithmic_bytes_per_launch"] = byts / 2
     roof["launch_gbs"] = {"gate_up": g1_bytes / gemm1_us / 1e3, "down": g2_bytes / gemm2_us / 1e3}
     roof["mfma_tflops"] = flops / t / 1e12
 
     # Every stage against its own roofline: algorithmic bytes (and flops) per
-    # launch, over the stage's event window (which includes ~2 us of dispatch
-    # latency, so the small launch-bound stages read low here; the committed
-    # kernel-trace summaries give the kernels' own durations).
+    # launch, over the stage's kernel duration (its event window less the
+    # marker cost, as above).
     R, T, nv, E = wl.rows, wl.topk, inp["num_valid"], wl.experts
     sH, sI = (H // 128) * sb, (I // 128) * sb
     row_in = 2 * H if std else H + sH   # a received row: bf16, or fp8 + scales
