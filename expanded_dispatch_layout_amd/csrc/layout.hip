@@ -411,8 +411,9 @@ __device__ __forceinline__ void quant_pass(const u32x4 (&v)[8], int c0, int nch,
 // receive buffer (into tot) and over the slots before `npre` (into pre), for
 // E <= 8: every workgroup of the fused launch runs this itself (at most
 // kFusedSlots slots, so 32-bit slot indices); tot and pre are cleared here.
-// The loads cover all `nall` slots of the buffer, so that they need not wait
-// for the valid-row bound; slots at or past `nslot` are not counted.  ids are
+// The first pass of loads covers the buffer's slots (up to 8 x NTH vectors)
+// whatever the valid-row bound, so that it need not wait for it; slots at or
+// past `nslot` are not counted.  ids are
 // read as 16-byte vectors when aligned (four slots each), eight in flight
 // per thread.
 // Each thread keeps its counts in 7-bit fields of a 64-bit word, expert e
@@ -452,9 +453,12 @@ __device__ __forceinline__ void count_all(const int32_t* __restrict__ ids, int n
   int done = 0;
   if (vec) {
     const int n4 = nall >> 2;
+    const int n4v = min(n4, (nslot + 3) >> 2);  // vectors holding valid slots
     const int4* ids4 = reinterpret_cast<const int4*>(ids);
     constexpr int U = 8;
-    for (int i0 = 0; i0 < n4; i0 += U * NTH) {
+    // (only the first pass reads past the valid slots: by the second the
+    // bound has arrived)
+    for (int i0 = 0; i0 < (i0 == 0 ? n4 : n4v); i0 += U * NTH) {
       int4 v[U];
 #pragma unroll
       for (int u = 0; u < U; ++u) {
