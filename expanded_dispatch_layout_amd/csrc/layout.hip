@@ -8,14 +8,16 @@
 // vLLM PR 54109 PaddedStandard (Motivation/Design: -1 slots, device-side
 // real/padding boundary, zeroed alignment gaps).
 //
-// Small receive buffers (rows * topk <= 65536 slots, rows copied as they
-// are: the DeepSeek-V3-shape share, the padded buffer, the decode share):
-// ONE launch.  Every 1024-thread workgroup reads the whole buffer's valid
-// ids itself (128 KB at the DeepSeek-V3 share, one round trip from L2) and
-// counts, per expert, all of them and those before its own 16-row group
-// (LDS atomics on the few local ids); it then scans the counts into the
-// aligned starts and psum (workgroup 0 writes them and the status) and
-// scatters its group, a wave per row.
+// Small receive buffers (rows * topk <= 65536 slots, at most 8 local
+// experts, rows copied as they are: the DeepSeek-V3-shape share, the padded
+// buffer, the decode share): ONE launch.  Every 1024-thread workgroup reads
+// the buffer's ids itself (128 KB at the DeepSeek-V3 share; the first pass
+// of loads is issued before the valid-row bound arrives) and counts, per
+// expert, the valid slots and those before its own 16-row group in 7-bit
+// per-thread fields, summed over each wave by a DPP transpose-reduce; it
+// requests its first row's data, scans the counts into the aligned starts
+// and psum (workgroup 0 writes them and the status) and scatters its group,
+// a wave per row.
 //
 // Larger buffers: up to three kernels on one stream (two when the block
 // table is small: every scatter workgroup then scans it itself):
@@ -40,9 +42,9 @@
 // start[e] + rank; the row (16-byte chunks) and its scales are read once and
 // written to each destination.  The same grid zero-fills the alignment pad
 // rows and writes the row labels (grid-stride), so no extra pass is needed.
-// Rows at or past the valid-row boundary are never read as routing: the
-// scatter (fused or not) does not load their ids, the count kernel ignores
-// the ones it loads with the rest of its block, and their slots get -1.
+// Rows at or past the valid-row boundary are never read as routing: their
+// ids are either not loaded or loaded with their neighbours and ignored, and
+// their slots get -1.
 //
 // bf16 input (the standard path, SGLang moe_runner/deep_gemm.py source,
 // pre_permute_standard_to_deep_gemm: per-token-group quantisation, then the
