@@ -18,6 +18,8 @@ benchmark times (ExpandedMoE, capacity from the host bound).
   empties three.
 * The padded buffers also check that a tail whose ids alias valid experts
   changes nothing.
+* `prefill_h6144` is the pages' prefill trace shape (18432 expanded rows of
+  H=6144).
 """
 
 import os
@@ -100,7 +102,7 @@ def check_all_rows(name, inp, L, I, out):
         assert np.all(out[nv:] == 7.0)                # past the boundary: untouched
 
 
-FULL = ["dsv3", "dsv3_zipf_ue8m0", "large", "padded", "padded_alias"]
+FULL = ["dsv3", "dsv3_zipf_ue8m0", "large", "padded", "padded_alias", "prefill_h6144"]
 STAGES = {"dsv3", "dsv3_zipf_ue8m0", "large"}
 
 

@@ -191,6 +191,25 @@ def test_layout_flags_and_bad_ids():
     assert ref["flags"] & layout.FLAG_EXPERT_ID_RANGE
 
 
+def test_layout_unaligned_ids():
+    """topk_ids 4 bytes past a 16-byte boundary (and 900 slots, not a
+    multiple of four): the single-launch count then reads the ids one slot at
+    a time instead of as 16-byte vectors."""
+    inp = make("tiny", rows=300, experts=6, global_experts=9, topk=3, align=16, seed=92)
+    g = to_gpu(inp)
+    R, T = inp["ids"].shape
+    base = torch.empty(R * T + 1, dtype=torch.int32, device="cuda")
+    ids = base[1:].view(R, T)
+    ids.copy_(g["ids"])
+    assert ids.data_ptr() % 16 != 0
+    mod = M.ExpandedMoE(R, T, g["w13"], g["w13_scale"], g["w2"], g["w2_scale"], inp["align"],
+                        inp["fmt"])
+    mod.ex.fill_(SENT)
+    mod.layout(g["x"], g["x_scale"], ids, g["w"], g["prank"])
+    torch.cuda.synchronize()
+    check_layout(mod, inp)
+
+
 def test_layout_duplicate_ids():
     inp = make("tiny", seed=91)
     ids = inp["ids"].copy()

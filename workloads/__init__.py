@@ -41,6 +41,11 @@ dsv3_decode        decode share on the masked slab: 1024 received rows
                    I=2048, 8 local of 256 experts, top-8 uniform,
                    alignment 128, fp32 scales, slab height max_m=128
                    (about four times the ~32 rows an expert expects)
+prefill_h6144      the pages' prefill trace shape: 16384 received rows,
+                   every one with a local slot, H=6144, I=2048, 8 local of
+                   256 experts, top-8, alignment 128, fp32 scales -> 18432
+                   expanded rows (their [~18432, 6144] activations and
+                   [~18432, 16] down-input scales)
 =================  =====================================================
 
 Recipe (numpy PCG64, seed 1000 + index): routing by Gumbel top-T over the
@@ -106,6 +111,8 @@ WORKLOADS = {
                            seed=1011),
     "dsv3_decode": Workload("dsv3_decode", 1024, 7168, 2048, 8, 256, 8, 128,
                             seed=1008, max_m=128),
+    "prefill_h6144": Workload("prefill_h6144", 16384, 6144, 2048, 8, 256, 8, 128,
+                              routing="local", seed=1012),
 }
 
 
