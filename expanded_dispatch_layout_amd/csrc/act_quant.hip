@@ -43,13 +43,19 @@ __global__ __launch_bounds__(kThreads) void act_quant_kernel(
     uint8_t* __restrict__ out_scale) {
   const int t = threadIdx.x, lane = t & 63;
   const int ngroups = inter / kGroup;
-  // Round trip 1: the total, this workgroup's first label and, with at most
-  // 64 experts, every expert's end (lane e holds psum[e]) together (the grid
-  // never exceeds the capacity, so row blockIdx.x is in bounds).
+  // Round trip 1: the total, this workgroup's first label and every
+  // expert's end together (the grid never exceeds the capacity, so row
+  // blockIdx.x is in bounds): with at most 64 experts lane e holds psum[e],
+  // with more the workgroup copies psum into LDS.
+  __shared__ int l_pe[kMasked ? 1 : MOE_MAX_EXPERTS];
   int64_t m = blockIdx.x;
   int e_next = kMasked ? 0 : m_indices[m];
   const bool psum_lanes = !kMasked && E <= 64;
   const int pl = psum_lanes && lane < E ? psum[lane] : 0;
+  if (!kMasked && !psum_lanes) {  // uniform
+    for (int e = t; e < E; e += kThreads) l_pe[e] = psum[e];
+    __syncthreads();
+  }
   const int64_t nrows = kMasked ? capacity : min((int64_t)status[0], capacity);
   for (; m < nrows; m += gridDim.x) {
     int e, pe;
@@ -62,15 +68,13 @@ __global__ __launch_bounds__(kThreads) void act_quant_kernel(
       if (m + gridDim.x < nrows) e_next = m_indices[m + gridDim.x];
       if (e < 0 || e >= E) continue;  // uniform per workgroup
     }
-    // Round trip 2: the fold weight and the row's first pass together (with
-    // more than 64 experts also the expert's end, and then a pad row's
-    // unwritten G values are loaded but never used; otherwise a pad row
-    // loads none).
-    if constexpr (!kMasked) pe = psum_lanes ? __shfl(pl, e, 64) : psum[e];
+    // Round trip 2: the fold weight and the row's first pass together (a
+    // pad row loads none).
+    if constexpr (!kMasked) pe = psum_lanes ? __shfl(pl, e, 64) : l_pe[e];
     const float w = kFold ? fold_w[m] : 1.f;
     const uint16_t* grow = gu + m * (int64_t)(2 * inter);
     u32x4 gv0 = {0u, 0u, 0u, 0u}, uv0 = {0u, 0u, 0u, 0u};
-    if (t * 8 < inter && (!psum_lanes || m < pe)) {
+    if (t * 8 < inter && m < pe) {
       gv0 = *reinterpret_cast<const u32x4*>(grow + t * 8);
       uv0 = *reinterpret_cast<const u32x4*>(grow + inter + t * 8);
     }
