@@ -59,8 +59,9 @@
 //  - UE8M0 scales: the exponent bytes are the MFMA's hardware scale operands
 //    (the group's byte repeats over its four 32-wide sub-blocks), so the
 //    matrix core accumulates the scaled products directly.
-//  - The bf16 outputs go straight from the accumulators to memory, 8 bytes
-//    (4 columns of one row) per lane and tile; rows past the group are never
+//  - The bf16 outputs pass through LDS (each wave's 64 x 64 tile in its own
+//    8 KB of the idle ring) so that every store instruction writes whole
+//    128-byte row segments; rows past the group's live rows are never
 //    written.
 //  - Masked mode (the decode path's fixed-height slab, SGLang
 //    moe_runner/deep_gemm.py source, _run_masked_gemm; SGLang PR 37261, "Why
