@@ -328,6 +328,44 @@ def test_stages_multi_group_experts(over):
                   label="multi-group")
 
 
+# The GEMM's epilogue (each wave's 64 x 64 tile staged in LDS, then whole
+# 128-byte row segments written for the live rows only): experts whose live
+# row counts end inside every row-tile position of a 256-row group, on
+# exact tile edges, one past them and across groups.
+EDGE_COUNTS = [1, 16, 17, 63, 65, 200, 257, 511]
+
+
+def test_gemm_epilogue_row_edges():
+    from tests._inputs import quantise
+    import workloads as W
+    R = sum(EDGE_COUNTS)
+    wl = W.workload("tiny", rows=R, hidden=1024, inter=512, experts=len(EDGE_COUNTS),
+                    global_experts=len(EDGE_COUNTS), topk=1, align=128, seed=94)
+    data = W.generate(wl)
+    ids = np.repeat(np.arange(len(EDGE_COUNTS), dtype=np.int32), EDGE_COUNTS)
+    np.random.default_rng(94).shuffle(ids)
+    data["ids"] = ids.reshape(R, 1)
+    inp = quantise(data)
+    L = _oracle_stage_inputs(inp)
+    assert list(L["counts"]) == EDGE_COUNTS
+    g = to_gpu(inp)
+    mod = M.ExpandedMoE(R, 1, g["w13"], g["w13_scale"], g["w2"], g["w2_scale"], inp["align"],
+                        inp["fmt"])
+    mod.layout(g["x"], g["x_scale"], g["ids"], g["w"], g["prank"])
+    check_stages(inp, L, g, mod, "row edges")
+    # Rows the GEMM must not write: alignment pads and the tail past the total.
+    mod.gate_up.view(torch.int16).fill_(0x7B7B)
+    M.moe_grouped_gemm_fp8(mod.ex, mod.ex_scale, inp["fmt"], mod.w13, mod.w13_scale, mod.psum,
+                           mod.status, inp["align"], mod.gate_up)
+    torch.cuda.synchronize()
+    raw = mod.gate_up.view(torch.int16).cpu().numpy()
+    live = L["live"]
+    n = min(L["total"], mod.capacity)
+    assert np.all(raw[:n][~live] == 0x7B7B)
+    assert np.all(raw[n:] == 0x7B7B)
+    assert not np.any(np.all(raw[:n][live] == 0x7B7B, axis=1))
+
+
 def _check_output(got, ref, scale=1.0, flipped=None, label=""):
     """The layer-output bars.
 
