@@ -857,8 +857,8 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(
     // Instead each wave passes its 64 x 64 tile through LDS (its own 8 KB of
     // the idle ring; 16-byte chunks XOR-swizzled by row) and writes whole
     // 128-byte row segments: 8 rows per store instruction, live rows only.
-    // (Measured: the step's two GEMMs 4 us faster at the DeepSeek-V3 share,
-    // 50 us at the prefill shape.)
+    // (Measured: the layer step 3 us faster at the DeepSeek-V3 share, 40 us
+    // at the prefill shape.)
     {
       const uint32_t stage = lds0 + (uint32_t)wid * 8192u;
       const int g = lane >> 4, f = lane & 15;
